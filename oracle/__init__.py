@@ -1,0 +1,139 @@
+"""fp64 CPU oracle of the (gated) delta rule -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never touches it, and the two share no code: this wraps
+``dn_oracle.c``, a plain token-by-token recurrence in double precision
+(Gated DeltaNet review thread, Table 1, rows "DeltaNet" / "Gated DeltaNet":
+S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t),
+its sequential adjoint, and a single recurrent step.
+
+Inputs may be torch tensors (any float dtype, on any device) or numpy arrays;
+they are upcast exactly to float64 on the host.  Results are float64 numpy.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dn_oracle.c")
+_LIB = os.path.join(_HERE, "_dn_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Returns the .so path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.oracle_fwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I]
+        lib.oracle_fwd.restype = I
+        lib.oracle_bwd.argtypes = [I, I, I, I, I, I, P] + [P] * 8 + [P] * 6 + [I]
+        lib.oracle_bwd.restype = I
+        lib.oracle_step.argtypes = [I, I, I, I, P, P, P, P, P, P, P, I]
+        lib.oracle_step.restype = I
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _i32(x):
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dims(q, v, cu):
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = (len(cu) - 1) if cu is not None else B
+    return B, T, H, Dk, Dv, N
+
+
+def fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, nthreads=0):
+    """Forward pass.  Returns (o [B,T,H,Dv], hT [N,H,Dk,Dv]) as float64."""
+    q, k, v, beta, g, h0 = map(_f64, (q, k, v, beta, g, h0))
+    cu = _i32(cu_seqlens)
+    B, T, H, Dk, Dv, N = _dims(q, v, cu)
+    o = np.zeros((B, T, H, Dv))
+    hT = np.zeros((N, H, Dk, Dv))
+    rc = _load().oracle_fwd(B, T, H, Dk, Dv, N, _ptr(cu), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(beta), _ptr(g), _ptr(h0), _ptr(o), _ptr(hT), int(nthreads))
+    if rc:
+        raise ValueError("oracle_fwd failed (%d)" % rc)
+    return o, hT
+
+
+def bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, nthreads=0):
+    """Backward pass of L = <dO, o> + <dhT, hT>.  Returns a dict with
+    dq, dk, dv, dbeta, dg (None if ungated) and dh0, all float64."""
+    q, k, v, beta, g, h0, dO, dhT = map(_f64, (q, k, v, beta, g, h0, dO, dhT))
+    cu = _i32(cu_seqlens)
+    B, T, H, Dk, Dv, N = _dims(q, v, cu)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dbeta = np.zeros_like(beta)
+    dg = np.zeros_like(beta) if g is not None else None
+    dh0 = np.zeros((N, H, Dk, Dv))
+    rc = _load().oracle_bwd(B, T, H, Dk, Dv, N, _ptr(cu), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(beta), _ptr(g), _ptr(h0), _ptr(dO), _ptr(dhT),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
+                            _ptr(dh0), int(nthreads))
+    if rc:
+        raise ValueError("oracle_bwd failed (%d)" % rc)
+    return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dh0=dh0)
+
+
+def step(q, k, v, beta, g, state, nthreads=0):
+    """One recurrent step.  q, k [B,H,Dk], v [B,H,Dv], beta/g [B,H],
+    state [B,H,Dk,Dv].  Returns (o [B,H,Dv], new_state) as float64."""
+    q, k, v, beta, g = map(_f64, (q, k, v, beta, g))
+    st = _f64(state).copy()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    o = np.zeros((B, H, Dv))
+    rc = _load().oracle_step(B, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                             _ptr(g), _ptr(st), _ptr(o), int(nthreads))
+    if rc:
+        raise ValueError("oracle_step failed (%d)" % rc)
+    return o, st

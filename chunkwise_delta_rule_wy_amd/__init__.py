@@ -1,0 +1,239 @@
+"""Chunkwise (gated) delta rule on AMD MI355X (gfx950).
+
+The recurrence (Gated DeltaNet review thread, Table 1, rows "DeltaNet" and
+"Gated DeltaNet"), per sequence and head:
+
+    S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+    o_t = S_t q_t,   alpha_t = exp(g_t)
+
+evaluated chunkwise in WY/UT form by hand-written HIP kernels in ``libdn.so``.
+This module is a thin ctypes binding: it checks tensors, allocates outputs and
+workspace with torch, and passes raw device pointers and the current HIP
+stream to the C ABI declared in ``include/dn.h``.  Every step of the
+computation runs in the library's kernels; there is no fallback.
+
+States are stored transposed, ``h = S^T`` with shape ``[N, H, Dk, Dv]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "DeltaRule", "delta_rule",
+           "load_library", "LIB_PATH", "DnError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")
+
+DN_F32, DN_BF16 = 0, 1
+_DTYPES = {torch.float32: DN_F32, torch.bfloat16: DN_BF16}
+
+
+class DnError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s: %s" % (fn, msg))
+        self.status = status
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libdn.so is not built (%s); run __graft_entry__.build() or "
+                           "python chunkwise_delta_rule_wy_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S = ctypes.c_void_p, ctypes.POINTER(_Shape)
+    lib.dn_status_str.argtypes = [ctypes.c_int]
+    lib.dn_status_str.restype = ctypes.c_char_p
+    lib.dn_chunk_fwd_workspace.argtypes = [S]
+    lib.dn_chunk_fwd_workspace.restype = ctypes.c_size_t
+    lib.dn_chunk_bwd_workspace.argtypes = [S]
+    lib.dn_chunk_bwd_workspace.restype = ctypes.c_size_t
+    lib.dn_chunk_fwd.argtypes = [S] + [P] * 9 + [P, ctypes.c_size_t, P]
+    lib.dn_chunk_fwd.restype = ctypes.c_int
+    lib.dn_chunk_bwd.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P, ctypes.c_size_t, P]
+    lib.dn_chunk_bwd.restype = ctypes.c_int
+    lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
+    lib.dn_recurrent_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = load_library().dn_status_str(status).decode()
+        raise DnError(fn, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, shape, dev):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _shape(q, v, cu_seqlens, chunk):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, Dk]")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    return _Shape(B, T, H, Dk, Dv, N, chunk, _DTYPES[q.dtype]), N
+
+
+def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_state=True,
+              chunk: int = 64):
+    """Chunkwise forward pass.
+
+    q, k ``[B,T,H,Dk]``, v ``[B,T,H,Dv]`` (float32 or bfloat16, one dtype);
+    beta, g ``[B,T,H]`` float32 (g None: no gate); h0 ``[N,H,Dk,Dv]`` float32
+    or None; cu_seqlens int32 ``[N+1]`` on the device for packed sequences
+    (then B == 1).  Returns ``(o, hT)`` (hT None unless output_final_state).
+    """
+    lib = load_library()
+    s, N = _shape(q, v, cu_seqlens, chunk)
+    dev = q.device
+    B, T, H, Dk, Dv = s.B, s.T, s.H, s.Dk, s.Dv
+    _need(q, "q", q.dtype, (B, T, H, Dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, Dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, Dv), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(g, "g", torch.float32, (B, T, H), dev)
+    _need(h0, "h0", torch.float32, (N, H, Dk, Dv), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    hT = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
+    wsb = lib.dn_chunk_fwd_workspace(ctypes.byref(s))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check("dn_chunk_fwd", lib.dn_chunk_fwd(
+        ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
+        _ptr(cu_seqlens), _ptr(o), _ptr(hT), _ptr(ws), wsb, _stream(dev)))
+    return o, hT
+
+
+def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 64,
+              workspace: Optional[torch.Tensor] = None):
+    """Backward pass of ``<dO, o> + <dhT, hT>``.
+
+    Returns a dict of float32 gradients dq, dk, dv, dbeta, dg (None without a
+    gate) and dh0.  ``workspace`` (uint8, at least ``bwd_workspace_bytes``)
+    may be passed to avoid an allocation per call.
+    """
+    lib = load_library()
+    s, N = _shape(q, v, cu_seqlens, chunk)
+    dev = q.device
+    B, T, H, Dk, Dv = s.B, s.T, s.H, s.Dk, s.Dv
+    _need(q, "q", q.dtype, (B, T, H, Dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, Dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, Dv), dev)
+    _need(dO, "dO", q.dtype, (B, T, H, Dv), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(g, "g", torch.float32, (B, T, H), dev)
+    _need(h0, "h0", torch.float32, (N, H, Dk, Dv), dev)
+    _need(dhT, "dhT", torch.float32, (N, H, Dk, Dv), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    dg = torch.empty((B, T, H), **f32) if g is not None else None
+    dh0 = torch.empty((N, H, Dk, Dv), **f32)
+    wsb = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check("dn_chunk_bwd", lib.dn_chunk_bwd(
+        ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
+        _ptr(cu_seqlens), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),
+        _ptr(dg), _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dh0=dh0)
+
+
+def bwd_workspace_bytes(B, T, H, Dk, Dv, n_seqs=None, dtype=torch.bfloat16, chunk=64) -> int:
+    s = _Shape(B, T, H, Dk, Dv, B if n_seqs is None else n_seqs, chunk, _DTYPES[dtype])
+    return int(load_library().dn_chunk_bwd_workspace(ctypes.byref(s)))
+
+
+def recurrent_step(q, k, v, beta, g, state):
+    """One decode step.  q, k ``[B,H,Dk]``, v ``[B,H,Dv]``, beta/g ``[B,H]``
+    float32 (g may be None), state ``[B,H,Dk,Dv]`` float32 updated in place.
+    Returns o ``[B,H,Dv]``."""
+    lib = load_library()
+    if q.dim() != 3 or q.dtype not in _DTYPES or q.device.type != "cuda":
+        raise ValueError("q must be a [B, H, Dk] float32/bfloat16 GPU tensor")
+    dev = q.device
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(q, "q", q.dtype, (B, H, Dk), dev)
+    _need(k, "k", q.dtype, (B, H, Dk), dev)
+    _need(v, "v", q.dtype, (B, H, Dv), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(g, "g", torch.float32, (B, H), dev)
+    _need(state, "state", torch.float32, (B, H, Dk, Dv), dev)
+    o = torch.empty((B, H, Dv), dtype=q.dtype, device=dev)
+    _check("dn_recurrent_step", lib.dn_recurrent_step(
+        B, H, Dk, Dv, _DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+        _ptr(state), _ptr(o), _stream(dev)))
+    return o
+
+
+class DeltaRule(torch.autograd.Function):
+    """Autograd wrapper: forward by ``chunk_fwd``, backward by ``chunk_bwd``.
+    Gradients are computed in float32 and cast to each input's dtype."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, g, h0, cu_seqlens):
+        o, hT = chunk_fwd(q, k, v, beta, g, h0, cu_seqlens, output_final_state=True)
+        ctx.save_for_backward(q, k, v, beta, g, h0, cu_seqlens)
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, dO, dhT):
+        q, k, v, beta, g, h0, cu = ctx.saved_tensors
+        if dO is None:
+            dO = torch.zeros(v.shape, dtype=q.dtype, device=q.device)
+        gr = chunk_bwd(q, k, v, beta, g, h0, dO.to(q.dtype).contiguous(),
+                       None if dhT is None else dhT.float().contiguous(), cu)
+        return (gr["dq"].to(q.dtype), gr["dk"].to(k.dtype), gr["dv"].to(v.dtype), gr["dbeta"],
+                gr["dg"], None if h0 is None else gr["dh0"], None)
+
+
+def delta_rule(q, k, v, beta, g=None, h0=None, cu_seqlens=None):
+    """Differentiable chunkwise (gated) delta rule; returns (o, hT)."""
+    return DeltaRule.apply(q, k, v, beta, g, h0, cu_seqlens)

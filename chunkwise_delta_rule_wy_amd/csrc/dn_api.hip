@@ -1,0 +1,229 @@
+// C ABI of the library: argument validation, workspace sizing and launches.
+// Every entry point validates on the host and enqueues nothing on error; it
+// never allocates, frees or synchronises.
+#include "dn.h"
+#include "dn_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == DN_BF16 ? 2 : 4; }
+
+dn_status check_shape(const dn_shape *s, const int32_t *cu) {
+  if (!s) return DN_EINVAL;
+  if (s->B <= 0 || s->T < 0 || s->H <= 0 || s->Dk <= 0 || s->Dv <= 0 || s->n_seqs <= 0)
+    return DN_EINVAL;
+  if (s->dtype != DN_F32 && s->dtype != DN_BF16) return DN_EINVAL;
+  if (cu) {
+    if (s->B != 1) return DN_EINVAL;
+  } else if (s->n_seqs != s->B) {
+    return DN_EINVAL;
+  }
+  if (s->chunk != 64) return DN_EUNSUPPORTED;
+  if (s->Dk != 64 && s->Dk != 128) return DN_EUNSUPPORTED;
+  if (s->Dv % 64 != 0 || s->Dv > 1024) return DN_EUNSUPPORTED;
+  if (s->dtype == DN_F32 && s->Dk != 64) return DN_EUNSUPPORTED;
+  // element offsets are computed in 64-bit, but grid and per-sequence counts are int
+  if ((int64_t)s->n_seqs * s->H * (s->Dv / 64) > (int64_t)1 << 30) return DN_EUNSUPPORTED;
+  return DN_OK;
+}
+
+// Upper bound on the number of 64-token chunks over all sequences.
+int64_t max_chunks(const dn_shape *s, bool varlen) {
+  if (!varlen) return (int64_t)s->B * ((s->T + 63) / 64);
+  // sum_n ceil(L_n / 64) <= floor(T / 64) + n_seqs
+  return (int64_t)s->T / 64 + s->n_seqs;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t states, dstates, table, total;
+};
+
+BwdLayout bwd_layout(const dn_shape *s, bool varlen) {
+  BwdLayout L;
+  const size_t nch = (size_t)max_chunks(s, varlen);
+  const size_t per = (size_t)s->H * s->Dk * s->Dv * sizeof(float);
+  L.states = 0;
+  L.dstates = align256(nch * per);
+  L.table = L.dstates + align256(nch * per);
+  L.total = L.table + (varlen ? align256(sizeof(int32_t) * ((size_t)s->n_seqs + 1 + nch)) : 0);
+  return L;
+}
+
+dn_status from_hip(hipError_t e) { return e == hipSuccess ? DN_OK : DN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *dn_status_str(dn_status s) {
+  switch (s) {
+    case DN_OK: return "DN_OK";
+    case DN_EINVAL: return "DN_EINVAL: invalid argument";
+    case DN_EUNSUPPORTED: return "DN_EUNSUPPORTED: shape or dtype not supported";
+    case DN_ENOWS: return "DN_ENOWS: workspace too small";
+    case DN_EHIP: return "DN_EHIP: HIP launch error";
+  }
+  return "unknown dn_status";
+}
+
+size_t dn_chunk_fwd_workspace(const dn_shape *s) {
+  (void)s;
+  return 0;
+}
+
+dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const void *v,
+                       const float *beta, const float *g, const float *h0,
+                       const int32_t *cu_seqlens, void *o, float *hT, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  dn_status st = check_shape(s, cu_seqlens);
+  if (st != DN_OK) return st;
+  (void)workspace;
+  (void)workspace_bytes;
+  if (s->T > 0) {
+    if (!q || !k || !v || !beta || !o) return DN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_EINVAL;
+  }
+  dn::FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g = g;
+  p.h0 = h0;
+  p.cu = cu_seqlens;
+  p.o = o;
+  p.hT = hT;
+  p.states = nullptr;
+  p.chunk_base = nullptr;
+  p.B = s->B;
+  p.T = s->T;
+  p.H = s->H;
+  p.DV = s->Dv;
+  p.N = s->n_seqs;
+  p.NC = (s->T + 63) / 64;
+  p.ntiles = s->Dv / 64;
+  p.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
+  return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, false, true, stream));
+}
+
+size_t dn_chunk_bwd_workspace(const dn_shape *s) {
+  if (!s || s->H <= 0 || s->Dk <= 0 || s->Dv <= 0 || s->B <= 0 || s->T < 0 || s->n_seqs <= 0)
+    return 0;
+  return bwd_layout(s, s->n_seqs != s->B || s->B == 1).total;
+}
+
+dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const void *v,
+                       const float *beta, const float *g, const float *h0,
+                       const int32_t *cu_seqlens, const void *dO, const float *dhT, float *dq,
+                       float *dk, float *dv, float *dbeta, float *dg, float *dh0, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  dn_status st = check_shape(s, cu_seqlens);
+  if (st != DN_OK) return st;
+  if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
+  const bool varlen = cu_seqlens != nullptr;
+  if (s->T > 0) {
+    if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return DN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+      return DN_EINVAL;
+  }
+  // the workspace query cannot see cu_seqlens, so it sizes for the varlen bound
+  const BwdLayout L = bwd_layout(s, varlen || s->B == 1);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return DN_ENOWS;
+  char *ws = static_cast<char *>(workspace);
+  const int64_t nchunks = max_chunks(s, varlen);
+  int32_t *chunk_base = nullptr, *chunk_seq = nullptr;
+  if (varlen) {
+    chunk_base = reinterpret_cast<int32_t *>(ws + L.table);
+    chunk_seq = chunk_base + s->n_seqs + 1;
+    hipError_t e = dn::launch_chunk_table(cu_seqlens, s->n_seqs, chunk_base, chunk_seq,
+                                          (int)nchunks, stream);
+    if (e != hipSuccess) return DN_EHIP;
+  }
+  float *states = reinterpret_cast<float *>(ws + L.states);
+  float *dstates = reinterpret_cast<float *>(ws + L.dstates);
+
+  // 1. forward sweep that stores every chunk-start state
+  dn::FwdParams fp = {};
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.beta = beta;
+  fp.g = g;
+  fp.h0 = h0;
+  fp.cu = cu_seqlens;
+  fp.o = nullptr;
+  fp.hT = nullptr;
+  fp.states = states;
+  fp.chunk_base = chunk_base;
+  fp.B = s->B;
+  fp.T = s->T;
+  fp.H = s->H;
+  fp.DV = s->Dv;
+  fp.N = s->n_seqs;
+  fp.NC = (s->T + 63) / 64;
+  fp.ntiles = s->Dv / 64;
+  fp.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
+  hipError_t e = dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
+  if (e != hipSuccess) return DN_EHIP;
+
+  // 2. reverse sweep for the state gradients, 3. chunk-parallel token gradients
+  dn::BwdParams bp = {};
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.dO = dO;
+  bp.beta = beta;
+  bp.g = g;
+  bp.dhT = dhT;
+  bp.cu = cu_seqlens;
+  bp.chunk_base = chunk_base;
+  bp.chunk_seq = chunk_seq;
+  bp.states = states;
+  bp.dstates = dstates;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dbeta = dbeta;
+  bp.dg = dg;
+  bp.dh0 = dh0;
+  bp.B = s->B;
+  bp.T = s->T;
+  bp.H = s->H;
+  bp.DV = s->Dv;
+  bp.N = s->n_seqs;
+  bp.NC = (s->T + 63) / 64;
+  bp.ntiles = s->Dv / 64;
+  bp.xcd_map = fp.xcd_map;
+  bp.total_chunks = (int)nchunks;
+  return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream));
+}
+
+dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                            const void *q, const void *k, const void *v, const float *beta,
+                            const float *g, float *state, void *o, hipStream_t stream) {
+  if (B <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return DN_EINVAL;
+  if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+  if (Dk != 64 && Dk != 128) return DN_EUNSUPPORTED;
+  if (Dv % 64 != 0 || Dv > 1024) return DN_EUNSUPPORTED;
+  if (!q || !k || !v || !beta || !state || !o) return DN_EINVAL;
+  if (!aligned16(state)) return DN_EINVAL;
+  dn::StepParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g = g;
+  p.state = state;
+  p.o = o;
+  p.B = B;
+  p.H = H;
+  p.DV = Dv;
+  return from_hip(dn::launch_step(p, dtype, Dk, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (dn_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dn_device.h"
+
+namespace dn {
+
+struct FwdParams {
+  const void *q, *k, *v;
+  const float *beta, *g, *h0;
+  const int32_t *cu;          // device offsets, or null for fixed length
+  void *o;                    // may be null when o is not written
+  float *hT;                  // may be null
+  float *states;              // chunk-start states [chunk][H][DK][DV] (backward only)
+  const int32_t *chunk_base;  // varlen: first global chunk of each sequence (backward only)
+  int B, T, H, DV, N, NC;     // NC: chunks per sequence for fixed length
+  int ntiles;                 // DV / 64
+  int xcd_map;                // 1 when (N * H) % 8 == 0
+};
+
+struct BwdParams {
+  const void *q, *k, *v, *dO;
+  const float *beta, *g, *dhT;
+  const int32_t *cu;
+  const int32_t *chunk_base;  // varlen: first global chunk of each sequence
+  const int32_t *chunk_seq;   // varlen: sequence of each global chunk
+  const float *states;        // chunk-start states
+  float *dstates;             // gradient w.r.t. each chunk's end state
+  float *dq, *dk, *dv, *dbeta, *dg, *dh0;
+  int B, T, H, DV, N, NC;
+  int ntiles, xcd_map;
+  int total_chunks;           // upper bound of chunks (grid of the chunk-parallel pass)
+};
+
+struct StepParams {
+  const void *q, *k, *v;
+  const float *beta, *g;
+  float *state;
+  void *o;
+  int B, H, DV;
+};
+
+size_t fwd_smem_bytes(int dtype, int DK);
+hipError_t launch_fwd(const FwdParams &p, int dtype, int DK, bool store_states, bool write_o,
+                      hipStream_t stream);
+hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
+hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
+                              int max_chunks, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream);
+size_t bwd_smem_bytes(int dtype, int DK);
+
+}  // namespace dn

@@ -1,0 +1,130 @@
+/*
+ * dn.h -- C ABI of the chunkwise (gated) delta-rule library for AMD MI355X
+ * (gfx950).  All device code behind these calls is hand-written HIP.
+ *
+ * The operation (Gated DeltaNet review thread, "Gated Delta Networks:
+ * Improving Mamba2 with Delta Rule", Table 1, rows "DeltaNet" and
+ * "Gated DeltaNet"), per sequence and head, token by token:
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * with S_t in R^{Dv x Dk}, alpha_t = exp(g_t) (alpha == 1 without a gate) and
+ * no query scaling.  The library evaluates it chunkwise: 64-token chunks whose
+ * products of Householder-like transitions are written in WY/UT form
+ * ("Parallelizing Linear Transformers with the Delta Rule over Sequence
+ * Length", page 3 abstract, and page 1 answers Q1/Q2), which is exact: results
+ * differ from the token loop only by floating-point rounding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees, or synchronises; each call enqueues its kernels on
+ *   `stream` and returns.  Inputs are read-only (except the decode `state`,
+ *   updated in place).  There is no global mutable state: calls are
+ *   thread-safe; calls sharing a workspace on different streams race.
+ * - Layouts are dense row-major:
+ *     q, k        [B, T, H, Dk]       v, o, dO    [B, T, H, Dv]
+ *     beta, g     [B, T, H]  fp32
+ *     h0, hT, dhT, dh0   [N, H, Dk, Dv]  fp32, holding h = S^T
+ *   N is the number of sequences: B, or n_seqs when `cu_seqlens` is given.
+ * - Packed variable-length input: `cu_seqlens` (device, int32 [n_seqs + 1],
+ *   non-decreasing, cu[0] = 0, cu[n_seqs] = T) requires B == 1; sequence n
+ *   covers tokens [cu[n], cu[n+1]) and chunks restart at every sequence start.
+ *   A zero-length sequence passes its h0 through to hT.  The library does not
+ *   copy cu_seqlens to the host; malformed offsets are undefined behaviour.
+ * - Validation happens on the host before any launch; on error nothing is
+ *   enqueued.  Kernel faults surface at the caller's next synchronisation.
+ * - Supported: Dk in {64, 128}; Dv a positive multiple of 64 up to 1024;
+ *   chunk == 64; dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
+ *   pointers 16-byte aligned.
+ */
+#ifndef DN_H_
+#define DN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DN_OK = 0,
+    DN_EINVAL = 1,       /* null required pointer, bad dims, misalignment, g/dg mismatch */
+    DN_EUNSUPPORTED = 2, /* valid but not implemented: Dk, Dv, chunk, dtype            */
+    DN_ENOWS = 3,        /* workspace smaller than the query function's answer          */
+    DN_EHIP = 4          /* a HIP launch reported an error                              */
+} dn_status;
+
+typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
+
+/* Problem shape.  For packed input B == 1, T is the total token count and
+ * n_seqs the number of sequences; otherwise n_seqs must equal B. */
+typedef struct {
+    int32_t B, T, H, Dk, Dv;
+    int32_t n_seqs;
+    int32_t chunk;   /* chunk length; 64 */
+    int32_t dtype;   /* dn_dtype of q, k, v, o, dO */
+} dn_shape;
+
+/* Human-readable name of a status code (static string). */
+const char *dn_status_str(dn_status s);
+
+/* Bytes of device workspace dn_chunk_fwd needs for this shape (may be 0). */
+size_t dn_chunk_fwd_workspace(const dn_shape *s);
+
+/*
+ * Chunkwise forward pass.  Produces o for every token and, if hT != NULL, the
+ * final state of every (sequence, head).  g == NULL means no gate (alpha = 1);
+ * h0 == NULL means a zero initial state.  The per-chunk WY/UT factors and the
+ * chunk-start states stay on chip; nothing but o and hT is written
+ * (Parallelizing Linear Transformers..., page 1, answer Q2, describes the
+ * materialise-then-recompute trade-off this pass avoids for inference).
+ */
+dn_status dn_chunk_fwd(const dn_shape *s,
+                       const void *q, const void *k, const void *v,
+                       const float *beta, const float *g, const float *h0,
+                       const int32_t *cu_seqlens,
+                       void *o, float *hT,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace dn_chunk_bwd needs for this shape. */
+size_t dn_chunk_bwd_workspace(const dn_shape *s);
+
+/*
+ * Chunkwise backward pass of L = <dO, o> + <dhT, hT> (dhT == NULL means 0).
+ * Recomputes the chunk-start states in a forward sweep (the recompute-in-the-
+ * backward design of Parallelizing Linear Transformers..., page 1, answer Q2),
+ * then runs a reverse sweep for the state gradients and a chunk-parallel pass
+ * for the token gradients.  Writes fp32 gradients in the input layouts:
+ * dq, dk [B,T,H,Dk], dv [B,T,H,Dv], dbeta [B,T,H], dg [B,T,H] (must be NULL
+ * exactly when g is NULL), dh0 [N,H,Dk,Dv] (NULL skips it).
+ */
+dn_status dn_chunk_bwd(const dn_shape *s,
+                       const void *q, const void *k, const void *v,
+                       const float *beta, const float *g, const float *h0,
+                       const int32_t *cu_seqlens,
+                       const void *dO, const float *dhT,
+                       float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One recurrent (decode) step for B x H independent states: the token update
+ * above applied once (Gated DeltaNet review thread, General Response 2: the
+ * recurrent step is memory-bound and its cost is set by the state size).
+ * q, k [B,H,Dk]; v, o [B,H,Dv] (dtype); beta, g [B,H] fp32 (g may be NULL);
+ * state [B,H,Dk,Dv] fp32 holding S^T, read and overwritten in place.
+ * Supported: Dk in {64, 128}, Dv a positive multiple of 64 up to 1024.
+ */
+dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,
+                            const void *q, const void *k, const void *v,
+                            const float *beta, const float *g,
+                            float *state, void *o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DN_H_ */

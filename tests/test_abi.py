@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function ``include/dn.h`` declares, and
+reject invalid arguments on the host with the documented status codes before
+it touches the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_delta_rule_wy_amd as dn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DN_OK, DN_EINVAL, DN_EUNSUPPORTED, DN_ENOWS, DN_EHIP = range(5)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"dn_chunk_fwd", "dn_chunk_bwd", "dn_recurrent_step", "dn_status_str",
+            "dn_chunk_fwd_workspace", "dn_chunk_bwd_workspace"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.dn_status_str(code).decode().startswith("DN_")
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def shape(**kw):
+    d = dict(B=2, T=128, H=2, Dk=64, Dv=64, n_seqs=2, chunk=64, dtype=1)
+    d.update(kw)
+    return dn._Shape(**d)
+
+
+def fwd(lib, s, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, h0=None, cu=None, o=FAKE, hT=None):
+    P = ctypes.c_void_p
+    return lib.dn_chunk_fwd(ctypes.byref(s), P(q), P(k), P(v), P(beta), P(g), P(h0), P(cu),
+                            P(o), P(hT), None, 0, None)
+
+
+def bwd(lib, s, g=None, dg=None, ws=FAKE, wsb=1 << 40, cu=None, q=FAKE):
+    P = ctypes.c_void_p
+    return lib.dn_chunk_bwd(ctypes.byref(s), P(q), P(FAKE), P(FAKE), P(FAKE), P(g), None, P(cu),
+                            P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(dg), None,
+                            P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), DN_EINVAL), (dict(H=0), DN_EINVAL), (dict(T=-1), DN_EINVAL),
+    (dict(Dk=0), DN_EINVAL), (dict(dtype=7), DN_EINVAL), (dict(n_seqs=3), DN_EINVAL),
+    (dict(chunk=32), DN_EUNSUPPORTED), (dict(Dk=96), DN_EUNSUPPORTED),
+    (dict(Dk=256), DN_EUNSUPPORTED), (dict(Dv=48), DN_EUNSUPPORTED),
+    (dict(Dv=2048), DN_EUNSUPPORTED), (dict(dtype=0, Dk=128), DN_EUNSUPPORTED),
+])
+def test_fwd_rejects_bad_shapes(lib, kw, code):
+    assert fwd(lib, shape(**kw)) == code
+
+
+def test_fwd_rejects_null_and_misaligned(lib):
+    assert fwd(lib, shape(), q=None) == DN_EINVAL
+    assert fwd(lib, shape(), beta=None) == DN_EINVAL
+    assert fwd(lib, shape(), o=None) == DN_EINVAL
+    assert fwd(lib, shape(), k=FAKE + 2) == DN_EINVAL
+    # packed sequences need B == 1
+    assert fwd(lib, shape(B=2, n_seqs=3), cu=FAKE) == DN_EINVAL
+
+
+def test_bwd_validation(lib):
+    s = shape()
+    assert bwd(lib, s, g=FAKE, dg=None) == DN_EINVAL
+    assert bwd(lib, s, g=None, dg=FAKE) == DN_EINVAL
+    assert bwd(lib, s, q=None) == DN_EINVAL
+    need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
+    assert need > 0
+    assert bwd(lib, s, wsb=need - 1) == DN_ENOWS
+    assert bwd(lib, s, ws=None) == DN_ENOWS
+    assert bwd(lib, shape(chunk=128)) == DN_EUNSUPPORTED
+
+
+def test_bwd_workspace_covers_varlen_bound(lib):
+    # packed input: sum ceil(L/64) <= T/64 + n_seqs chunks of H*Dk*Dv fp32
+    s1 = shape(B=1, T=1000, n_seqs=7)
+    per = 2 * 64 * 64 * 4
+    assert lib.dn_chunk_bwd_workspace(ctypes.byref(s1)) >= 2 * (1000 // 64 + 7) * per
+
+
+def test_step_validation(lib):
+    P = ctypes.c_void_p
+    f = lib.dn_recurrent_step
+    assert f(0, 1, 64, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert f(1, 1, 96, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED
+    assert f(1, 1, 64, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE), None) == DN_EINVAL
+    assert f(1, 1, 64, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE + 4), P(FAKE), None) == DN_EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        dn.chunk_fwd(q, q, q, torch.zeros(1, 64, 1))

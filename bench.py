@@ -1,0 +1,226 @@
+"""Benchmark of the chunkwise gated delta rule on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+A step is one pass of the hot path over one batch of seeded synthetic input
+already resident in HBM: for the default workload (gated delta rule, bf16,
+B=4 T=4096 H=16 dk=128 dv=256) that is the chunkwise forward pass plus the
+chunkwise backward pass (dq, dk, dv, dbeta, dg, dh0).  Workloads 2, 3 and 5
+are forward-only; "dec" is one decode step at batch 256, H=32, d=128.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline position of
+the forward kernel (timed live with HIP events on the launch stream), and the
+fp64 oracle's throughput on a bounded sample of the same workload on the host
+cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
+
+
+def workload_bytes(sh, backward: bool) -> float:
+    """Algorithmic HBM bytes: one read of every input, one write of every
+    output, at their dtypes (no intermediate counted)."""
+    es = 2 if str(sh.dtype).endswith("bfloat16") else 4
+    th = sh.B * sh.T * sh.H
+    st = sh.n_seqs * sh.H * sh.Dk * sh.Dv * 4
+    fwd = th * (2 * sh.Dk * es + 2 * sh.Dv * es + 4 * (2 if sh.gated else 1))
+    fwd += st * ((1 if sh.has_h0 else 0) + 1)
+    if not backward:
+        return float(fwd)
+    bwd = th * (2 * sh.Dk * es + 2 * sh.Dv * es + 4 * (2 if sh.gated else 1)   # q k v dO beta g
+                + 2 * sh.Dk * 4 + sh.Dv * 4 + 4 * (2 if sh.gated else 1))      # dq dk dv dbeta dg
+    bwd += st * (1 + 1 + 1)                                                    # h0 dhT dh0
+    return float(fwd + bwd)
+
+
+def fwd_flops(sh) -> float:
+    """Algorithmic flops of the chunkwise forward pass as this library
+    evaluates it (triangular products at their exact half), per token-head:
+    K K^T strict (C-1)/2 dk, Q K^T (C+1)/2 dk, (I+A)^-1 C^2/6,
+    T X and P V' (C+1)/2 dv each, K h, Q h, K^T V' dk dv each (MACs)."""
+    C, dk, dv = 64, sh.Dk, sh.Dv
+    mac = (C - 1) / 2 * dk + (C + 1) / 2 * dk + C * C / 6 + (C + 1) * dv + 3 * dk * dv
+    return 2.0 * mac * sh.B * sh.T * sh.H
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every (sequence, head) pair is independent; see DESIGN.md for sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunkwise_delta_rule_wy_amd as dn
+    from chunkwise_delta_rule_wy_amd import synth
+
+    dev = torch.device("cuda:0")
+    wid = args.workload
+    if wid == "dec":
+        return bench_decode(args, dn, synth, dev)
+    wid = int(wid)
+    sh = synth.WORKLOADS[wid]
+    backward = sh.backward
+    x = synth.workload_inputs(wid)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    torch.cuda.synchronize()
+
+    ws = None
+    if backward:
+        ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv, sh.n_seqs,
+                                                sh.dtype), dtype=torch.uint8, device=dev)
+
+    def step():
+        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+        if backward:
+            dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
+                         d["cu_seqlens"], workspace=ws)
+        return o
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / max(args.steps, 1)
+    tokens = sh.B * sh.T
+    value = tokens / (ms_per_step * 1e-3)
+
+    # the forward kernel alone, timed with HIP events on its launch stream
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    nf = max(args.steps, 5)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(nf):
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+    ev1.record(stream)
+    ev1.synchronize()
+    fwd_us = ev0.elapsed_time(ev1) * 1e3 / nf
+    fbytes = workload_bytes(sh, False)
+    achieved = fbytes / (fwd_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "dn::fwd_kernel", "kernel_us": round(fwd_us, 2),
+                "bytes_per_launch": fbytes,
+                "tflops": round(fwd_flops(sh) / (fwd_us * 1e-6) / 1e12, 2)}
+
+    out = {
+        "metric": "tokens/s & TFLOP/s (fraction of MFMA peak), gated delta-rule fwd+bwd",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded, L2-normalised q/k, sigmoid beta, -softplus*0.1 gate)",
+        "config": {"workload": synth.WORKLOAD_NAMES[wid], "B": sh.B, "T": sh.T, "H": sh.H,
+                   "Dk": sh.Dk, "Dv": sh.Dv, "chunk": 64, "passes": "fwd+bwd" if backward else "fwd",
+                   "n_seqs": sh.n_seqs},
+        "roofline": roofline,
+        "step_gbs": round(workload_bytes(sh, backward) / (ms_per_step * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x, sh, backward, budget_s):
+    """The fp64 oracle on a bounded sample: whole sequences of a few heads."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    nthr = int(os.environ.get("OMP_NUM_THREADS", cores) or cores)
+    nthr = max(1, min(nthr, cores))
+    # sample: the first `npairs` (batch, head) pairs over the full sequence
+    # length; grow until the budget is roughly used
+    npairs, elapsed, T = nthr, 0.0, sh.T
+    while True:
+        b_idx = [i // sh.H for i in range(npairs)]
+        h_idx = [i % sh.H for i in range(npairs)]
+        import torch
+        sel = lambda t: torch.stack([t[b, :, h] for b, h in zip(b_idx, h_idx)], 0).unsqueeze(2)
+        xs = dict(q=sel(x["q"]), k=sel(x["k"]), v=sel(x["v"]), beta=sel(x["beta"]),
+                  g=None if x["g"] is None else sel(x["g"]))
+        h0 = None if x["h0"] is None else torch.stack([x["h0"][b, h] for b, h in zip(b_idx, h_idx)]).unsqueeze(1)
+        if sh.lengths is not None:
+            # packed input: sample whole heads of the first sequence
+            L = sh.lengths[0]
+            xs = {k: (v[:, :L] if v is not None else None) for k, v in xs.items()}
+            h0 = h0[:, :1] if h0 is not None else None
+            T = L
+        t0 = time.perf_counter()
+        oracle.fwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, nthreads=nthr)
+        if backward:
+            dO = sel(x["dO"])
+            dhT = torch.stack([x["dhT"][b, h] for b, h in zip(b_idx, h_idx)]).unsqueeze(1)
+            oracle.bwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, dO, dhT, nthreads=nthr)
+        elapsed = time.perf_counter() - t0
+        if elapsed * 4 > budget_s or npairs >= sh.B * sh.H:
+            break
+        npairs = min(npairs * 4, sh.B * sh.H)
+    token_heads = npairs * T
+    return {"value": round(token_heads / sh.H / elapsed, 1), "unit": "tokens/s",
+            "cores": nthr, "kind": "oracle",
+            "sample": "%d (batch, head) pairs x %d tokens (%s), %.1f s; tokens/s counts a token "
+                      "as all %d heads" % (npairs, T, "fwd+bwd" if backward else "fwd", elapsed, sh.H)}
+
+
+def bench_decode(args, dn, synth, dev):
+    import torch
+    x = synth.decode_inputs()
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    st = d["state"]
+    for _ in range(args.warmup):
+        dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], st)
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], st)
+    ev1.record(stream)
+    ev1.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    B, H, Dk, Dv = 256, 32, 128, 128
+    nbytes = B * H * Dk * Dv * 4 * 2 + B * H * (2 * Dk + 2 * Dv) * 2 + B * H * 8
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({"metric": "decode step", "value": round(B / (us * 1e-6), 1),
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic", "config": {"workload": "decode-B256-H32-d128"},
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "traffic": None}}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,16 +6,14 @@
 // An f32 accumulator tile (f32x4) holds rows 4g + i (i = 0..3) of column n:
 // this is the MFMA output layout on CDNA.
 //
-// A contraction block of 32 indices is split so that lane group g owns the
-// 8 indices {4g + i, 16 + 4g + i : i = 0..3}.  Two stacked accumulator tiles
-// (rows 0..15 and 16..31 of a matrix whose rows are the contraction index) are
-// therefore already a B operand in registers -- no shuffles, no LDS round
-// trip.  The A operand is read from a row-major matrix as two 4-element runs
-// per lane.  The hardware sums over every (lane group, element) pair, so any
-// fixed index assignment is exact as long as A and B share it.
+// A contraction block of 32 indices gives lane group g the 8 indices
+// 8g .. 8g + 7 (one 16-byte bf16 read of an A row).  Which physical index each
+// (group, element) slot stands for is free as long as A and B agree: the
+// hardware sums over every slot.  dn_chunk.h fixes the row order of the
+// accumulator tiles so that two stacked tiles are a B operand in registers.
 //
-// A 16-index block (16x16x16 products) uses indices {4g + i}: one accumulator
-// tile is a B operand as is.
+// A 16-index block (16x16x16 products) gives lane group g the indices
+// 4g .. 4g + 3: one accumulator tile is a B operand as is.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,7 +68,7 @@ __device__ __forceinline__ f32x4 mma16(f32x4 c, f32x4 a, f32x4 b) {
 template <typename E> __device__ __forceinline__ E to_e(float x) { return (E)x; }
 template <typename E> __device__ __forceinline__ float to_f(E x) { return (float)x; }
 
-// B fragment (32-index block) from two accumulator tiles, each value scaled
+// B fragment (32-index block) from two stacked accumulator tiles
 template <typename E>
 __device__ __forceinline__ F32<E> bfrag(const f32x4 &lo, const f32x4 &hi) {
   F32<E> r;
@@ -98,44 +96,6 @@ template <> struct four<float> {
   typedef f32x4 type;
 };
 
-// A fragment (32-index block kb) of row `row` of a row-major LDS matrix
-template <typename E>
-__device__ __forceinline__ F32<E> afrag(const E *m, int ld, int row, int kb) {
-  const int g = lane_id() >> 4;
-  const E *p = m + row * ld + kb * 32 + 4 * g;
-  typedef typename four<E>::type V4;
-  V4 lo = *reinterpret_cast<const V4 *>(p);
-  V4 hi = *reinterpret_cast<const V4 *>(p + 16);
-  F32<E> r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = lo[i];
-    r[4 + i] = hi[i];
-  }
-  return r;
-}
-// A fragment (16-index block starting at column c0)
-template <typename E>
-__device__ __forceinline__ F16<E> afrag16(const E *m, int ld, int row, int c0) {
-  const int g = lane_id() >> 4;
-  typedef typename four<E>::type V4;
-  V4 v = *reinterpret_cast<const V4 *>(m + row * ld + c0 + 4 * g);
-  F16<E> r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = v[i];
-  return r;
-}
-// A fragment (16-index block) from an fp32 row-major LDS matrix, converted
-template <typename E>
-__device__ __forceinline__ F16<E> afrag16_f(const float *m, int ld, int row, int c0) {
-  const int g = lane_id() >> 4;
-  f32x4 v = *reinterpret_cast<const f32x4 *>(m + row * ld + c0 + 4 * g);
-  F16<E> r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = to_e<E>(v[i]);
-  return r;
-}
-
 // 16 bytes of raw data
 struct alignas(16) u128 {
   uint32_t w[4];
@@ -155,6 +115,17 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wait states between an MFMA and VALU / memory reads of its result when the
+// two are separated by control flow.  CDNA does not interlock these reads
+// against the matrix pipeline; the compiler's hazard recognizer covers
+// straight-line code but has been seen to miss a taken branch between the
+// producer and the reader.  24 wait states exceed the longest (16-pass) case.
+__device__ __forceinline__ void mfma_settle() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -4,61 +4,57 @@
 // that sequence's 64-token chunks in order, keeping its slice of the state
 // h = S^T (d_k x 64, fp32) in registers the whole time.  Per chunk:
 //
-//   load     K, Q (64 x d_k), V tile (64 x 64), beta, g -> LDS (prefetched
-//            into registers one chunk ahead); b = cumsum(g), gamma = exp(b)
+//   load     K, Q (64 x d_k) and the V tile (64 x 64) arrive by direct
+//            global->LDS loads issued one chunk ahead into a second buffer;
+//            b = cumsum(g), gamma = exp(b), and K^T is formed in LDS
 //   phase A  A = strictLower(diag(beta) (K K^T) * Gamma),  P = (Q K^T) * Gamma
-//            (Gamma_rj = exp(b_r - b_j), j <= r), MFMA, 5 tiles per wave
-//   phase B  wave 0: R = (I + A)^-1 -- 16x16 diagonal blocks by forward
-//            substitution in fp32 registers, off-diagonal blocks by small MFMA
-//            products R_ij = -R_ii sum_m A_im R_mj -- and T = R diag(beta);
-//            meanwhile every wave forms Y_K = K h and Y_Q = Q h for its columns
+//            with Gamma_rj = exp(b_r - b_j) for j <= r (MFMA, 5 tiles a wave)
+//   phase B  R = (I + A)^-1, T = R diag(beta): 16x16 diagonal blocks by fp32
+//            forward substitution, off-diagonal blocks R_ij = -R_ii sum_m
+//            A_im R_mj by small MFMAs; every wave computes what its block row
+//            of T needs, overlapped with Y_K = K h and Y_Q = Q h
 //   phase C  X = V - diag(gamma) Y_K,  V' = T X,
 //            O = diag(gamma) Y_Q + P V',
 //            h <- gamma_64 h + K^T diag(exp(b_64 - b)) V'
 //
-// This is the WY/UT form of the chunk (products of Householder-like
-// transitions, "Parallelizing Linear Transformers with the Delta Rule over
-// Sequence Length", page 3 abstract; the UT transform is named in the Gated
+// This is the WY/UT form of a chunk ("Parallelizing Linear Transformers with
+// the Delta Rule over Sequence Length": products of Householder-like
+// transitions in WY form, page 3 abstract; the UT transform named in the Gated
 // DeltaNet review thread, review 2), with the gate entering through
 // cumulative decay ratios (page 1, answer W2).  Each wave owns 16 of the 64
 // d_v columns for the whole state chain, so the chain needs no cross-wave
 // exchange: only read-only operands (K, Q, K^T, T, P) are shared through LDS.
-//
 // Partial chunks are zero-padded rows (k = q = v = 0, beta = g = 0), which
 // leave A, T, V', gamma_64 and the state unchanged.
+#include "dn_chunk.h"
 #include "dn_internal.h"
 
 namespace dn {
 
 template <typename E, int DK>
-struct FwdSmem {
-  static constexpr int PAD = 16 / sizeof(E);  // 16-byte row skew
-  static constexpr int LDK = DK + PAD;        // K, Q rows
-  static constexpr int LD64 = 64 + PAD;       // 64-wide E matrices
-  static constexpr int LDA = 64 + 4;          // fp32 A
-  static constexpr int LDR = 16 + PAD;        // R diagonal blocks
-  E K[CH * LDK];
-  E Q[CH * LDK];
-  E KT[DK * LD64];
-  E V[CH * LD64];
-  E T[CH * LD64];
-  E P[CH * LD64];
-  E Rd[4 * 16 * LDR];
-  float A[CH * LDA];
-  float b[CH];
-  float gam[CH];
-  float beta[CH];
+struct FwdCfg {
+  static constexpr int NBUF = sizeof(E) == 2 ? 2 : 1;  // fp32 tiles fit LDS only once
+  static constexpr int KB = DK / 32;                   // 32-index blocks over d_k
+  static constexpr int MTK = DK / 16;                  // state row tiles per wave
+  static constexpr int LDA = 64 + 4;                   // fp32 A (padded)
+  static constexpr int LDT = 16 + 4;                   // fp32 diagonal blocks of A^T
+  static constexpr int LDR = sizeof(E) == 2 ? 20 : 16; // per-wave R blocks
 };
 
 template <typename E, int DK>
-struct Prefetch {
-  static constexpr int EPU = 16 / sizeof(E);         // elements per 16-byte unit
-  static constexpr int UK = DK / EPU;                // units per K row
-  static constexpr int NUK = CH * UK / NTHR;         // K units per thread
-  static constexpr int UV = DVT / EPU;               // units per V row
-  static constexpr int NUV = CH * UV / NTHR;         // V units per thread
-  u128 k[NUK], q[NUK], v[NUV];
-  float s;  // wave 0: g of row lane; wave 1: beta of row lane
+struct FwdSmem {
+  using C = FwdCfg<E, DK>;
+  E K[C::NBUF][CH * DK];
+  E Q[C::NBUF][CH * DK];
+  E V[C::NBUF][CH * DVT];
+  E KT[DK * CH];
+  E T[CH * CH];
+  E P[CH * CH];
+  float A[CH * C::LDA];
+  float ATd[4][16 * C::LDT];
+  E Rr[4][4][16 * C::LDR];  // per wave: diagonal R blocks, row-major
+  E Rc[4][4][16 * C::LDR];  // per wave: diagonal R blocks, column-major
+  Gates G[2];
 };
 
 struct SeqInfo {
@@ -79,13 +75,12 @@ __device__ __forceinline__ SeqInfo seq_info(const int32_t *cu, int n, int T) {
   return s;
 }
 
-// (seq, head, tile) of this workgroup; siblings of one (seq, head) land on one
-// XCD (workgroups are dealt to the 8 XCDs round-robin) so that their shared
-// K/Q reads hit the same L2.
-__device__ __forceinline__ void wg_coords(int x, int pairs, int ntiles, int xcd_map, int &pair,
-                                          int &tile) {
+// (pair, tile) of a workgroup.  Workgroups are dealt to the 8 XCDs round
+// robin; the d_v tiles of one (sequence, head) share K and Q, so they are
+// placed on one XCD (one L2).
+__device__ __forceinline__ void wg_coords(int x, int ntiles, int xcd_map, int &pair, int &tile) {
   if (xcd_map) {
-    int xcd = x & 7, slot = x >> 3;
+    const int xcd = x & 7, slot = x >> 3;
     pair = (slot / ntiles) * 8 + xcd;
     tile = slot % ntiles;
   } else {
@@ -94,319 +89,407 @@ __device__ __forceinline__ void wg_coords(int x, int pairs, int ntiles, int xcd_
   }
 }
 
+// K^T (d_k x 64) from the swizzled K tile: each thread moves a 4-row x
+// 16-byte block.
 template <typename E, int DK>
-__device__ __forceinline__ void prefetch_chunk(Prefetch<E, DK> &pf, const FwdParams &p, const SeqInfo &si,
-                                               int h, int dv0, int c, int L) {
-  using PF = Prefetch<E, DK>;
-  const int t = threadIdx.x;
-  const E *q = static_cast<const E *>(p.q);
-  const E *k = static_cast<const E *>(p.k);
-  const E *v = static_cast<const E *>(p.v);
-  const size_t tok0 = (size_t)si.b * p.T + si.t0 + (size_t)c * CH;
+__device__ __forceinline__ void build_kt(E *KT, const E *K) {
+  using TK = Tile<E, DK>;
+  using TT = Tile<E, CH>;
+  constexpr int EPU = TK::EPU;
+  constexpr int NBLK = (CH / 4) * TK::U;
+  for (int blk = threadIdx.x; blk < NBLK; blk += NTHR) {
+    const int rq = blk / TK::U, u = blk % TK::U;
+    E v[4][EPU];
 #pragma unroll
-  for (int i = 0; i < PF::NUK; ++i) {
-    int s = t + NTHR * i, row = s / PF::UK, cu = s % PF::UK;
-    if (row < L) {
-      size_t off = ((tok0 + row) * p.H + h) * DK + cu * PF::EPU;
-      pf.k[i] = ldg128(k + off);
-      pf.q[i] = ldg128(q + off);
-    } else {
-      pf.k[i] = zero128();
-      pf.q[i] = zero128();
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u128 *>(v[i]) = *reinterpret_cast<const u128 *>(K + TK::unit_off(4 * rq + i, u));
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      const int row = u * EPU + e;  // d_k index
+      typename four<E>::type col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) col[i] = v[i][e];
+      *reinterpret_cast<typename four<E>::type *>(KT + TT::off(row, 4 * rq)) = col;
     }
   }
-#pragma unroll
-  for (int i = 0; i < PF::NUV; ++i) {
-    int s = t + NTHR * i, row = s / PF::UV, cu = s % PF::UV;
-    if (row < L)
-      pf.v[i] = ldg128(v + ((tok0 + row) * p.H + h) * p.DV + dv0 + cu * PF::EPU);
-    else
-      pf.v[i] = zero128();
-  }
-  const int w = t >> 6, l = t & 63;
-  pf.s = 0.f;
-  if (l < L) {
-    size_t si_ = (tok0 + l) * p.H + h;
-    if (w == 0 && p.g) pf.s = p.g[si_];
-    if (w == 1) pf.s = p.beta[si_];
-  }
 }
 
-template <typename E, int DK>
-__device__ __forceinline__ void store_chunk(FwdSmem<E, DK> &sm, const Prefetch<E, DK> &pf) {
-  using PF = Prefetch<E, DK>;
-  using SM = FwdSmem<E, DK>;
-  const int t = threadIdx.x;
+// Phase A for one wave role: lower tiles of K K^T (ISK) or Q K^T, two tile
+// rows per wave (ODD: rows 1 and 2, else rows 0 and 3, five tiles either
+// way), each scaled by the gate ratios.  A (strict, times beta_r) goes to LDS
+// in fp32, plus the transposed diagonal blocks; P (inclusive) in E.  The
+// epilogue is straight-line code with selects only.
+template <typename E, int DK, bool GATED, bool ISK, bool ODD>
+__device__ __forceinline__ void phase_a_role(FwdSmem<E, DK> &sm, const E *Kc, const E *src,
+                                             const Gates &G) {
+  using C = FwdCfg<E, DK>;
+  using TT = Tile<E, CH>;
+  const int l = lane_id(), n = l & 15, g = l >> 4;
 #pragma unroll
-  for (int i = 0; i < PF::NUK; ++i) {
-    int s = t + NTHR * i, row = s / PF::UK, cu = s % PF::UK;
-    *reinterpret_cast<u128 *>(&sm.K[row * SM::LDK + cu * PF::EPU]) = pf.k[i];
-    *reinterpret_cast<u128 *>(&sm.Q[row * SM::LDK + cu * PF::EPU]) = pf.q[i];
-    const E *ke = reinterpret_cast<const E *>(&pf.k[i]);
+  for (int t = 0; t < 5; ++t) {
+    const int ti = ODD ? (t < 2 ? 1 : 2) : (t < 1 ? 0 : 3);
+    const int tj = ODD ? (t < 2 ? t : t - 2) : (t < 1 ? 0 : t - 1);
+    F32<E> a[C::KB], bq[C::KB];
 #pragma unroll
-    for (int e = 0; e < PF::EPU; ++e) sm.KT[(cu * PF::EPU + e) * SM::LD64 + row] = ke[e];
-  }
+    for (int kb = 0; kb < C::KB; ++kb) {
+      a[kb] = frag<E, DK>(src, 16 * ti + n, kb);
+      bq[kb] = frag<E, DK>(Kc, 16 * tj + n, kb);
+    }
+    f32x4 acc = zero4();
 #pragma unroll
-  for (int i = 0; i < PF::NUV; ++i) {
-    int s = t + NTHR * i, row = s / PF::UV, cu = s % PF::UV;
-    *reinterpret_cast<u128 *>(&sm.V[row * SM::LD64 + cu * PF::EPU]) = pf.v[i];
-  }
-  const int w = t >> 6, l = t & 63;
-  if (w == 0) {
-    float bsum = wave_incl_scan(pf.s);
-    sm.b[l] = bsum;
-    sm.gam[l] = __expf(bsum);
-  } else if (w == 1) {
-    sm.beta[l] = pf.s;
-  }
-}
-
-// Phase A: lower tiles of K K^T (waves 0, 1) and Q K^T (waves 2, 3), scaled by
-// the gate ratios; A (strict, times beta_r) in fp32, P (inclusive) in E.
-template <typename E, int DK>
-__device__ __forceinline__ void phase_a(FwdSmem<E, DK> &sm, bool gated) {
-  using SM = FwdSmem<E, DK>;
-  const int w = wave_id(), l = lane_id(), n = l & 15, g = l >> 4;
-  const E *src = (w < 2) ? sm.K : sm.Q;
-  const int rb0 = (w & 1) ? 1 : 0, rb1 = (w & 1) ? 2 : 3;
+    for (int kb = 0; kb < C::KB; ++kb) acc = mma32(acc, a[kb], bq[kb]);
+    const int j = 16 * tj + n;
+    const float bj = G.b[j];
+    const f32x4 br = *reinterpret_cast<const f32x4 *>(&G.b[16 * ti + 4 * g]);
+    const f32x4 be = *reinterpret_cast<const f32x4 *>(&G.beta[16 * ti + 4 * g]);
+    f32x4 outv;
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const int ti = which ? rb1 : rb0;
-    F32<E> af[DK / 32];
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) af[kb] = afrag<E>(src, SM::LDK, 16 * ti + n, kb);
-    for (int tj = 0; tj <= ti; ++tj) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb)
-        acc = mma32(acc, af[kb], afrag<E>(sm.K, SM::LDK, 16 * tj + n, kb));
-      const int j = 16 * tj + n;
-      const float bj = sm.b[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * ti + 4 * g + e;
-        const float gr = (gated && j <= r) ? __expf(sm.b[r] - bj) : 1.f;
-        if (w < 2) {
-          sm.A[r * SM::LDA + j] = (j < r) ? sm.beta[r] * gr * acc[e] : 0.f;
-        } else {
-          sm.P[r * SM::LD64 + j] = to_e<E>((j <= r) ? gr * acc[e] : 0.f);
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ti + 4 * g + e;
+      const float gr = GATED ? __expf(j <= r ? br[e] - bj : 0.f) : 1.f;
+      if (ISK) {
+        outv[e] = (j < r) ? be[e] * gr * acc[e] : 0.f;
+        sm.A[r * C::LDA + j] = outv[e];
+      } else {
+        sm.P[TT::off(r, j)] = to_e<E>((j <= r) ? gr * acc[e] : 0.f);
       }
     }
+    if (ISK && ti == tj) *reinterpret_cast<f32x4 *>(&sm.ATd[ti][n * C::LDT + 4 * g]) = outv;
   }
 }
 
-// Phase B (wave 0 only): T = (I + A)^-1 diag(beta) into sm.T.
+template <typename E, int DK, bool GATED, bool NEED_P>
+__device__ __forceinline__ void phase_a(FwdSmem<E, DK> &sm, const E *Kc, const E *Qc, const Gates &G) {
+  const int w = wave_id();
+  if (w == 0) phase_a_role<E, DK, GATED, true, false>(sm, Kc, Kc, G);
+  else if (w == 1) phase_a_role<E, DK, GATED, true, true>(sm, Kc, Kc, G);
+  else if (NEED_P && w == 2) phase_a_role<E, DK, GATED, false, false>(sm, Kc, Qc, G);
+  else if (NEED_P && w == 3) phase_a_role<E, DK, GATED, false, true>(sm, Kc, Qc, G);
+}
+
+// Phase B part 1 (every wave): the four 16x16 diagonal blocks of
+// R = (I + A)^-1 by fp32 forward substitution, lane (bi, c) computing
+// column c of block bi; the blocks go to this wave's scratch in both
+// layouts, and the wave's own diagonal block of T = R diag(beta) to sm.T.
 template <typename E, int DK>
-__device__ __forceinline__ void invert_wave0(FwdSmem<E, DK> &sm) {
-  using SM = FwdSmem<E, DK>;
-  const int l = lane_id(), bi = l >> 4, c = l & 15, g = l >> 4, n = l & 15;
-  // diagonal blocks: lane (bi, c) computes column c of (I + A_ii)^-1
-  float Rc[16];
+__device__ __forceinline__ void invert_diag(FwdSmem<E, DK> &sm, const Gates &G) {
+  using C = FwdCfg<E, DK>;
+  using TT = Tile<E, CH>;
+  const int w = wave_id(), l = lane_id(), bi = l >> 4, c = l & 15;
+  float x[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float acc = (r == c) ? 1.f : 0.f;
-    const float *arow = &sm.A[(16 * bi + r) * SM::LDA + 16 * bi];
+  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+  const float *at = sm.ATd[bi];
 #pragma unroll
-    for (int j = 0; j < r; ++j) acc -= arow[j] * Rc[j];
-    Rc[r] = acc;
+  for (int j = 0; j < 15; ++j) {
+    // column j of A_bi (rows > j): x[r] -= A[r][j] x[j]
+    f32x4 colv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) colv[q] = *reinterpret_cast<const f32x4 *>(at + j * C::LDT + 4 * q);
+#pragma unroll
+    for (int r = j + 1; r < 16; ++r) x[r] -= colv[r >> 2][r & 3] * x[j];
   }
-  const float bc = sm.beta[16 * bi + c];
+  E *rr = sm.Rr[w][bi];
+  E *rc = sm.Rc[w][bi];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    sm.Rd[(bi * 16 + r) * SM::LDR + c] = to_e<E>(Rc[r]);
-    sm.T[(16 * bi + r) * SM::LD64 + 16 * bi + c] = to_e<E>(Rc[r] * bc);
+  for (int r = 0; r < 16; ++r) rr[r * C::LDR + c] = to_e<E>(x[r]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    typename four<E>::type v4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] = to_e<E>(x[4 * q + i]);
+    *reinterpret_cast<typename four<E>::type *>(rc + c * C::LDR + 4 * q) = v4;
   }
-  wave_lds_fence();
-  // B fragment of diagonal block R_jj (column n, rows 4g..4g+3)
-  auto bdiag = [&](int j) {
+  if (bi == w) {
+    const float bc = G.beta[16 * w + c];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.T[TT::off(16 * w + r, 16 * w + c)] = to_e<E>(x[r] * bc);
+  }
+}
+
+// Phase B part 2: off-diagonal blocks of R that wave W's block row of T
+// needs (wave W writes T_W0 .. T_W,W-1), by 16x16x16 products:
+// R_ij = -R_ii sum_{m=j}^{i-1} A_im R_mj.  Straight-line code per wave.
+template <typename E, int DK, int W>
+__device__ __forceinline__ void invert_offdiag_w(FwdSmem<E, DK> &sm, const Gates &G) {
+  using C = FwdCfg<E, DK>;
+  using TT = Tile<E, CH>;
+  const int l = lane_id(), n = l & 15, g = l >> 4;
+  const E *rr = &sm.Rr[W][0][0];
+  const E *rc = &sm.Rc[W][0][0];
+  constexpr int BS = 16 * C::LDR;
+  auto ablk = [&](int i, int k) {  // A_ik rows, fp32 -> E
+    f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.A[(16 * i + n) * C::LDA + 16 * k + 4 * g]);
     F16<E> f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = sm.Rd[(j * 16 + 4 * g + i) * SM::LDR + n];
+    for (int e = 0; e < 4; ++e) f[e] = to_e<E>(v[e]);
     return f;
   };
-  auto ablk = [&](int i, int m) { return afrag16_f<E>(sm.A, SM::LDA, 16 * i + n, 16 * m); };
-  auto adiag = [&](int i) { return afrag16<E>(&sm.Rd[i * 16 * SM::LDR], SM::LDR, n, 0); };
+  auto adiag = [&](int i) {  // rows of R_ii
+    return *reinterpret_cast<const F16<E> *>(rr + i * BS + n * C::LDR + 4 * g);
+  };
+  auto bdiag = [&](int j) {  // columns of R_jj (rows 4g..4g+3 of column n)
+    return *reinterpret_cast<const F16<E> *>(rc + j * BS + n * C::LDR + 4 * g);
+  };
+  auto put = [&](int i, int j, const f32x4 &R) {
+    const float bj = G.beta[16 * j + n];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.T[TT::off(16 * i + 4 * g + e, 16 * j + n)] = to_e<E>(R[e] * bj);
+  };
   f32x4 y;
   y = mma16(zero4(), ablk(1, 0), bdiag(0));
   const f32x4 R10 = -mma16(zero4(), adiag(1), bfrag16<E>(y));
-  y = mma16(zero4(), ablk(2, 1), bdiag(1));
-  const f32x4 R21 = -mma16(zero4(), adiag(2), bfrag16<E>(y));
-  y = mma16(zero4(), ablk(3, 2), bdiag(2));
-  const f32x4 R32 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
-  y = mma16(zero4(), ablk(2, 0), bdiag(0));
-  y = mma16(y, ablk(2, 1), bfrag16<E>(R10));
-  const f32x4 R20 = -mma16(zero4(), adiag(2), bfrag16<E>(y));
-  y = mma16(zero4(), ablk(3, 1), bdiag(1));
-  y = mma16(y, ablk(3, 2), bfrag16<E>(R21));
-  const f32x4 R31 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
-  y = mma16(zero4(), ablk(3, 0), bdiag(0));
-  y = mma16(y, ablk(3, 1), bfrag16<E>(R10));
-  y = mma16(y, ablk(3, 2), bfrag16<E>(R20));
-  const f32x4 R30 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
-  auto put = [&](int i, int j, const f32x4 &R) {
-    const float bj = sm.beta[16 * j + n];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.T[(16 * i + 4 * g + e) * SM::LD64 + 16 * j + n] = to_e<E>(R[e] * bj);
-  };
-  put(1, 0, R10);
-  put(2, 1, R21);
-  put(3, 2, R32);
-  put(2, 0, R20);
-  put(3, 1, R31);
-  put(3, 0, R30);
+  if constexpr (W == 1) {
+    put(1, 0, R10);
+  } else {
+    y = mma16(zero4(), ablk(2, 1), bdiag(1));
+    const f32x4 R21 = -mma16(zero4(), adiag(2), bfrag16<E>(y));
+    y = mma16(zero4(), ablk(2, 0), bdiag(0));
+    y = mma16(y, ablk(2, 1), bfrag16<E>(R10));
+    const f32x4 R20 = -mma16(zero4(), adiag(2), bfrag16<E>(y));
+    if constexpr (W == 2) {
+      put(2, 0, R20);
+      put(2, 1, R21);
+    } else {
+      y = mma16(zero4(), ablk(3, 2), bdiag(2));
+      const f32x4 R32 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
+      y = mma16(zero4(), ablk(3, 1), bdiag(1));
+      y = mma16(y, ablk(3, 2), bfrag16<E>(R21));
+      const f32x4 R31 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
+      y = mma16(zero4(), ablk(3, 0), bdiag(0));
+      y = mma16(y, ablk(3, 1), bfrag16<E>(R10));
+      y = mma16(y, ablk(3, 2), bfrag16<E>(R20));
+      const f32x4 R30 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
+      put(3, 0, R30);
+      put(3, 1, R31);
+      put(3, 2, R32);
+    }
+  }
 }
 
-template <typename E, int DK, bool STORE_STATES, bool WRITE_O>
+template <typename E, int DK>
+__device__ __forceinline__ void invert_offdiag(FwdSmem<E, DK> &sm, const Gates &G) {
+  const int w = wave_id();
+  if (w == 1) invert_offdiag_w<E, DK, 1>(sm, G);
+  else if (w == 2) invert_offdiag_w<E, DK, 2>(sm, G);
+  else if (w == 3) invert_offdiag_w<E, DK, 3>(sm, G);
+}
+
+template <typename E, int DK, bool GATED, bool STORE_STATES, bool WRITE_O>
 __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
+  using C = FwdCfg<E, DK>;
   using SM = FwdSmem<E, DK>;
+  using TV = Tile<E, DVT>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SM &sm = *reinterpret_cast<SM *>(smem_raw);
-  constexpr int MT = DK / 16;  // state row tiles per wave
 
   int pair, tile;
-  wg_coords(blockIdx.x, p.N * p.H, p.ntiles, p.xcd_map, pair, tile);
+  wg_coords(blockIdx.x, p.ntiles, p.xcd_map, pair, tile);
   if (pair >= p.N * p.H) return;
   const int n_seq = pair / p.H, h = pair % p.H;
   const int dv0 = tile * DVT;
   const SeqInfo si = seq_info(p.cu, n_seq, p.T);
   const int nch = (si.len + CH - 1) / CH;
-  const bool gated = p.g != nullptr;
+  const E *gq = static_cast<const E *>(p.q);
+  const E *gk = static_cast<const E *>(p.k);
+  const E *gv = static_cast<const E *>(p.v);
+  E *go = static_cast<E *>(p.o);
 
   const int w = wave_id(), l = lane_id(), n = l & 15, g = l >> 4;
   const int col = dv0 + 16 * w + n;  // this lane's d_v column
+  const size_t row_base = (size_t)si.b * p.T + si.t0;  // global row of the sequence start
 
-  // zero T and P once: their upper triangles are never written again
-  for (int i = threadIdx.x; i < CH * SM::LD64; i += NTHR) {
+  // T and P: upper triangles stay zero
+  for (int i = threadIdx.x; i < CH * CH; i += NTHR) {
     sm.T[i] = to_e<E>(0.f);
     sm.P[i] = to_e<E>(0.f);
   }
 
-  // state slice: rows 16*mt + 4g + e, column `col`
-  f32x4 hacc[MT];
+  // state slice: lane (n, g) holds rows prow(mt, 4g + i) of column `col`
+  f32x4 hacc[C::MTK];
   const size_t st_base = ((size_t)n_seq * p.H + h) * DK * p.DV;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = 0; mt < C::MTK; ++mt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      hacc[mt][e] = p.h0 ? p.h0[st_base + (size_t)(16 * mt + 4 * g + e) * p.DV + col] : 0.f;
-  }
+    for (int i = 0; i < 4; ++i)
+      hacc[mt][i] = p.h0 ? p.h0[st_base + (size_t)prow(mt, 4 * g + i) * p.DV + col] : 0.f;
 
-  Prefetch<E, DK> pf;
-  if (nch > 0) prefetch_chunk<E, DK>(pf, p, si, h, dv0, 0, min(CH, si.len));
+  // scalar inputs of a chunk: wave 0 holds g, wave 1 holds beta of row `l`
+  auto load_scalars = [&](int c) {
+    const int L = min(CH, si.len - c * CH);
+    float s = 0.f;
+    if (l < L) {
+      const size_t idx = (row_base + (size_t)c * CH + l) * p.H + h;
+      if (GATED && w == 0) s = p.g[idx];
+      if (w == 1) s = p.beta[idx];
+    }
+    return s;
+  };
+  auto issue_loads = [&](int c, int buf) {
+    const int L = min(CH, si.len - c * CH);
+    const size_t r0 = row_base + (size_t)c * CH;
+    dma_tile<E, DK>(sm.K[buf], gk, r0, p.H, h, DK, 0, L);
+    if (WRITE_O) dma_tile<E, DK>(sm.Q[buf], gq, r0, p.H, h, DK, 0, L);
+    dma_tile<E, DVT>(sm.V[buf], gv, r0, p.H, h, p.DV, dv0, L);
+  };
+
+  float sc = 0.f;
+  if (nch > 0) {
+    issue_loads(0, 0);
+    sc = load_scalars(0);
+  }
+  typename four<E>::type ov[4];  // output of the previous chunk, stored one iteration late
+  int prevL = 0;
+  size_t prev_r0 = 0;
 
   for (int c = 0; c < nch; ++c) {
+    const int cur = C::NBUF == 2 ? (c & 1) : 0;
     const int L = min(CH, si.len - c * CH);
-    __syncthreads();
-    store_chunk<E, DK>(sm, pf);
-    __syncthreads();
-    if (c + 1 < nch) prefetch_chunk<E, DK>(pf, p, si, h, dv0, c + 1, min(CH, si.len - (c + 1) * CH));
+    const E *Kc = sm.K[cur];
+    const E *Qc = sm.Q[cur];
+    const E *Vc = sm.V[cur];
+    Gates &G = sm.G[c & 1];
+    wait_vmem();
+    if (WRITE_O && c > 0) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = prow(mt, 4 * g + i);
+          if (r < prevL) go[((prev_r0 + r) * p.H + h) * p.DV + col] = ov[mt][i];
+        }
+    }
+    if (L < CH) {
+      zero_rows<E, DK>(sm.K[cur], L);
+      if (WRITE_O) zero_rows<E, DK>(sm.Q[cur], L);
+      zero_rows<E, DVT>(sm.V[cur], L);
+    }
+    write_gates(G, w == 0 ? sc : 0.f, w == 1 ? sc : 0.f);
+    __syncthreads();  // chunk c visible; every wave is done with chunk c-1
+
+    if (c + 1 < nch) {
+      if (C::NBUF == 2) issue_loads(c + 1, cur ^ 1);
+      sc = load_scalars(c + 1);
+    }
     if (STORE_STATES) {
       const int cg = p.chunk_base ? p.chunk_base[n_seq] + c : n_seq * p.NC + c;
       float *dst = p.states + ((size_t)cg * p.H + h) * DK * p.DV;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < C::MTK; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * mt + 4 * g + e) * p.DV + col] = hacc[mt][e];
+        for (int i = 0; i < 4; ++i) dst[(size_t)prow(mt, 4 * g + i) * p.DV + col] = hacc[mt][i];
     }
-
-    phase_a<E, DK>(sm, gated);
+    build_kt<E, DK>(sm.KT, Kc);
+    phase_a<E, DK, GATED, WRITE_O>(sm, Kc, Qc, G);
     __syncthreads();
 
-    if (w == 0) invert_wave0<E, DK>(sm);
-    // Y_K = K h, Y_Q = Q h for this wave's 16 columns
-    F32<E> hb[DK / 32];
+    // phase B: UT inverse overlapped with Y_K = K h, Y_Q = Q h
+    F32<E> hb[C::KB];
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) hb[kb] = bfrag<E>(hacc[2 * kb], hacc[2 * kb + 1]);
+    for (int kb = 0; kb < C::KB; ++kb) hb[kb] = bfrag<E>(hacc[2 * kb], hacc[2 * kb + 1]);
     f32x4 yk[4], yq[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      yk[mt] = zero4();
-      yq[mt] = zero4();
+      F32<E> af[C::KB];
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        yk[mt] = mma32(yk[mt], afrag<E>(sm.K, SM::LDK, 16 * mt + n, kb), hb[kb]);
-        if (WRITE_O) yq[mt] = mma32(yq[mt], afrag<E>(sm.Q, SM::LDK, 16 * mt + n, kb), hb[kb]);
+      for (int kb = 0; kb < C::KB; ++kb) af[kb] = frag<E, DK>(Kc, prow(mt, n), kb);
+      yk[mt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) yk[mt] = mma32(yk[mt], af[kb], hb[kb]);
+    }
+    invert_diag<E, DK>(sm, G);
+    if (WRITE_O) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        F32<E> af[C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) af[kb] = frag<E, DK>(Qc, prow(mt, n), kb);
+        yq[mt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) yq[mt] = mma32(yq[mt], af[kb], hb[kb]);
       }
     }
+    wave_lds_fence();
+    invert_offdiag<E, DK>(sm, G);
+    mfma_settle();  // Y_K, Y_Q and the inverse are read after the barrier
     __syncthreads();
 
-    // X = V - diag(gamma) Y_K
-    f32x4 x[4];
+    // phase C
+    f32x4 x[4], gm[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      gm[mt] = *reinterpret_cast<const f32x4 *>(&G.gam[prow(mt, 4 * g)]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * mt + 4 * g + e;
-        x[mt][e] = to_f<E>(sm.V[r * SM::LD64 + 16 * w + n]) - sm.gam[r] * yk[mt][e];
+      for (int i = 0; i < 4; ++i) {
+        const int r = prow(mt, 4 * g + i);
+        x[mt][i] = to_f<E>(Vc[TV::off(r, 16 * w + n)]) - gm[mt][i] * yk[mt][i];
       }
-    F32<E> xb[2];
-    xb[0] = bfrag<E>(x[0], x[1]);
-    xb[1] = bfrag<E>(x[2], x[3]);
-    // V' = T X
+    }
+    F32<E> xb[2] = {bfrag<E>(x[0], x[1]), bfrag<E>(x[2], x[3])};
     f32x4 vp[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      vp[mt] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) vp[mt] = mma32(vp[mt], afrag<E>(sm.T, SM::LD64, 16 * mt + n, kb), xb[kb]);
+      const F32<E> a0 = frag<E, CH>(sm.T, prow(mt, n), 0);
+      const F32<E> a1 = frag<E, CH>(sm.T, prow(mt, n), 1);
+      vp[mt] = mma32(mma32(zero4(), a0, xb[0]), a1, xb[1]);
     }
-    F32<E> vb[2];
-    vb[0] = bfrag<E>(vp[0], vp[1]);
-    vb[1] = bfrag<E>(vp[2], vp[3]);
+    F32<E> vb[2] = {bfrag<E>(vp[0], vp[1]), bfrag<E>(vp[2], vp[3])};
+    f32x4 wvp[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 wl = *reinterpret_cast<const f32x4 *>(&G.wl[prow(mt, 4 * g)]);
+      wvp[mt] = wl * vp[mt];
+    }
+    F32<E> wb[2] = {bfrag<E>(wvp[0], wvp[1]), bfrag<E>(wvp[2], wvp[3])};
     if (WRITE_O) {
-      // O = diag(gamma) Y_Q + P V'
-      E *o = static_cast<E *>(p.o);
-      const size_t tok0 = (size_t)si.b * p.T + si.t0 + (size_t)c * CH;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc;
+        const F32<E> a0 = frag<E, CH>(sm.P, prow(mt, n), 0);
+        const F32<E> a1 = frag<E, CH>(sm.P, prow(mt, n), 1);
+        f32x4 acc = gm[mt] * yq[mt];
+        acc = mma32(mma32(acc, a0, vb[0]), a1, vb[1]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = sm.gam[16 * mt + 4 * g + e] * yq[mt][e];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc = mma32(acc, afrag<E>(sm.P, SM::LD64, 16 * mt + n, kb), vb[kb]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * mt + 4 * g + e;
-          if (r < L) o[((tok0 + r) * p.H + h) * p.DV + col] = to_e<E>(acc[e]);
-        }
+        for (int i = 0; i < 4; ++i) ov[mt][i] = to_e<E>(acc[i]);
       }
+      prevL = L;
+      prev_r0 = row_base + (size_t)c * CH;
     }
-    // h <- gamma_64 h + K^T diag(exp(b_64 - b)) V'
-    const float blast = sm.b[CH - 1];
-    const float glast = sm.gam[CH - 1];
-    f32x4 wv[4];
+    const float glast = G.gam[CH - 1];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * mt + 4 * g + e;
-        wv[mt][e] = (gated ? __expf(blast - sm.b[r]) : 1.f) * vp[mt][e];
-      }
-    F32<E> wb[2];
-    wb[0] = bfrag<E>(wv[0], wv[1]);
-    wb[1] = bfrag<E>(wv[2], wv[3]);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = hacc[mt] * glast;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) acc = mma32(acc, afrag<E>(sm.KT, SM::LD64, 16 * mt + n, kb), wb[kb]);
-      hacc[mt] = acc;
+    for (int mt = 0; mt < C::MTK; ++mt) {
+      const F32<E> a0 = frag<E, CH>(sm.KT, prow(mt, n), 0);
+      const F32<E> a1 = frag<E, CH>(sm.KT, prow(mt, n), 1);
+      hacc[mt] = mma32(mma32(hacc[mt] * glast, a0, wb[0]), a1, wb[1]);
+    }
+    mfma_settle();  // the state is read again across the loop edge
+    if (C::NBUF == 1 && c + 1 < nch) {
+      __syncthreads();  // single buffer: every wave is done reading chunk c
+      issue_loads(c + 1, 0);
     }
   }
 
+  if (WRITE_O && nch > 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = prow(mt, 4 * g + i);
+        if (r < prevL) go[((prev_r0 + r) * p.H + h) * p.DV + col] = ov[mt][i];
+      }
+  }
   if (p.hT) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < C::MTK; ++mt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p.hT[st_base + (size_t)(16 * mt + 4 * g + e) * p.DV + col] = hacc[mt][e];
+      for (int i = 0; i < 4; ++i) p.hT[st_base + (size_t)prow(mt, 4 * g + i) * p.DV + col] = hacc[mt][i];
   }
 }
 
 template <typename E, int DK, bool STORE_STATES, bool WRITE_O>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
   const size_t smem = sizeof(FwdSmem<E, DK>);
-  auto kern = fwd_kernel<E, DK, STORE_STATES, WRITE_O>;
+  auto kern = p.g ? fwd_kernel<E, DK, true, STORE_STATES, WRITE_O>
+                  : fwd_kernel<E, DK, false, STORE_STATES, WRITE_O>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;

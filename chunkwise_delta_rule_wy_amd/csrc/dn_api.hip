@@ -124,6 +124,7 @@ dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const vo
   dn_status st = check_shape(s, cu_seqlens);
   if (st != DN_OK) return st;
   if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
+  if (s->dtype != DN_BF16) return DN_EUNSUPPORTED;  // the backward kernels are bf16
   const bool varlen = cu_seqlens != nullptr;
   if (s->T > 0) {
     if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return DN_EINVAL;

@@ -26,8 +26,8 @@
 // exchange: only read-only operands (K, Q, K^T, T, P) are shared through LDS.
 // Partial chunks are zero-padded rows (k = q = v = 0, beta = g = 0), which
 // leave A, T, V', gamma_64 and the state unchanged.
-#include "dn_chunk.h"
 #include "dn_internal.h"
+#include "dn_prep.h"
 
 namespace dn {
 
@@ -36,9 +36,6 @@ struct FwdCfg {
   static constexpr int NBUF = sizeof(E) == 2 ? 2 : 1;  // fp32 tiles fit LDS only once
   static constexpr int KB = DK / 32;                   // 32-index blocks over d_k
   static constexpr int MTK = DK / 16;                  // state row tiles per wave
-  static constexpr int LDA = 64 + 4;                   // fp32 A (padded)
-  static constexpr int LDT = 16 + 4;                   // fp32 diagonal blocks of A^T
-  static constexpr int LDR = sizeof(E) == 2 ? 20 : 16; // per-wave R blocks
 };
 
 template <typename E, int DK>
@@ -50,10 +47,7 @@ struct FwdSmem {
   E KT[DK * CH];
   E T[CH * CH];
   E P[CH * CH];
-  float A[CH * C::LDA];
-  float ATd[4][16 * C::LDT];
-  E Rr[4][4][16 * C::LDR];  // per wave: diagonal R blocks, row-major
-  E Rc[4][4][16 * C::LDR];  // per wave: diagonal R blocks, column-major
+  PrepScratch<E> ps;
   Gates G[2];
 };
 
@@ -89,192 +83,6 @@ __device__ __forceinline__ void wg_coords(int x, int ntiles, int xcd_map, int &p
   }
 }
 
-// K^T (d_k x 64) from the swizzled K tile: each thread moves a 4-row x
-// 16-byte block.
-template <typename E, int DK>
-__device__ __forceinline__ void build_kt(E *KT, const E *K) {
-  using TK = Tile<E, DK>;
-  using TT = Tile<E, CH>;
-  constexpr int EPU = TK::EPU;
-  constexpr int NBLK = (CH / 4) * TK::U;
-  for (int blk = threadIdx.x; blk < NBLK; blk += NTHR) {
-    const int rq = blk / TK::U, u = blk % TK::U;
-    E v[4][EPU];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u128 *>(v[i]) = *reinterpret_cast<const u128 *>(K + TK::unit_off(4 * rq + i, u));
-#pragma unroll
-    for (int e = 0; e < EPU; ++e) {
-      const int row = u * EPU + e;  // d_k index
-      typename four<E>::type col;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) col[i] = v[i][e];
-      *reinterpret_cast<typename four<E>::type *>(KT + TT::off(row, 4 * rq)) = col;
-    }
-  }
-}
-
-// Phase A for one wave role: lower tiles of K K^T (ISK) or Q K^T, two tile
-// rows per wave (ODD: rows 1 and 2, else rows 0 and 3, five tiles either
-// way), each scaled by the gate ratios.  A (strict, times beta_r) goes to LDS
-// in fp32, plus the transposed diagonal blocks; P (inclusive) in E.  The
-// epilogue is straight-line code with selects only.
-template <typename E, int DK, bool GATED, bool ISK, bool ODD>
-__device__ __forceinline__ void phase_a_role(FwdSmem<E, DK> &sm, const E *Kc, const E *src,
-                                             const Gates &G) {
-  using C = FwdCfg<E, DK>;
-  using TT = Tile<E, CH>;
-  const int l = lane_id(), n = l & 15, g = l >> 4;
-#pragma unroll
-  for (int t = 0; t < 5; ++t) {
-    const int ti = ODD ? (t < 2 ? 1 : 2) : (t < 1 ? 0 : 3);
-    const int tj = ODD ? (t < 2 ? t : t - 2) : (t < 1 ? 0 : t - 1);
-    F32<E> a[C::KB], bq[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      a[kb] = frag<E, DK>(src, 16 * ti + n, kb);
-      bq[kb] = frag<E, DK>(Kc, 16 * tj + n, kb);
-    }
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) acc = mma32(acc, a[kb], bq[kb]);
-    const int j = 16 * tj + n;
-    const float bj = G.b[j];
-    const f32x4 br = *reinterpret_cast<const f32x4 *>(&G.b[16 * ti + 4 * g]);
-    const f32x4 be = *reinterpret_cast<const f32x4 *>(&G.beta[16 * ti + 4 * g]);
-    f32x4 outv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * ti + 4 * g + e;
-      const float gr = GATED ? __expf(j <= r ? br[e] - bj : 0.f) : 1.f;
-      if (ISK) {
-        outv[e] = (j < r) ? be[e] * gr * acc[e] : 0.f;
-        sm.A[r * C::LDA + j] = outv[e];
-      } else {
-        sm.P[TT::off(r, j)] = to_e<E>((j <= r) ? gr * acc[e] : 0.f);
-      }
-    }
-    if (ISK && ti == tj) *reinterpret_cast<f32x4 *>(&sm.ATd[ti][n * C::LDT + 4 * g]) = outv;
-  }
-}
-
-template <typename E, int DK, bool GATED, bool NEED_P>
-__device__ __forceinline__ void phase_a(FwdSmem<E, DK> &sm, const E *Kc, const E *Qc, const Gates &G) {
-  const int w = wave_id();
-  if (w == 0) phase_a_role<E, DK, GATED, true, false>(sm, Kc, Kc, G);
-  else if (w == 1) phase_a_role<E, DK, GATED, true, true>(sm, Kc, Kc, G);
-  else if (NEED_P && w == 2) phase_a_role<E, DK, GATED, false, false>(sm, Kc, Qc, G);
-  else if (NEED_P && w == 3) phase_a_role<E, DK, GATED, false, true>(sm, Kc, Qc, G);
-}
-
-// Phase B part 1 (every wave): the four 16x16 diagonal blocks of
-// R = (I + A)^-1 by fp32 forward substitution, lane (bi, c) computing
-// column c of block bi; the blocks go to this wave's scratch in both
-// layouts, and the wave's own diagonal block of T = R diag(beta) to sm.T.
-template <typename E, int DK>
-__device__ __forceinline__ void invert_diag(FwdSmem<E, DK> &sm, const Gates &G) {
-  using C = FwdCfg<E, DK>;
-  using TT = Tile<E, CH>;
-  const int w = wave_id(), l = lane_id(), bi = l >> 4, c = l & 15;
-  float x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-  const float *at = sm.ATd[bi];
-#pragma unroll
-  for (int j = 0; j < 15; ++j) {
-    // column j of A_bi (rows > j): x[r] -= A[r][j] x[j]
-    f32x4 colv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) colv[q] = *reinterpret_cast<const f32x4 *>(at + j * C::LDT + 4 * q);
-#pragma unroll
-    for (int r = j + 1; r < 16; ++r) x[r] -= colv[r >> 2][r & 3] * x[j];
-  }
-  E *rr = sm.Rr[w][bi];
-  E *rc = sm.Rc[w][bi];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) rr[r * C::LDR + c] = to_e<E>(x[r]);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    typename four<E>::type v4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v4[i] = to_e<E>(x[4 * q + i]);
-    *reinterpret_cast<typename four<E>::type *>(rc + c * C::LDR + 4 * q) = v4;
-  }
-  if (bi == w) {
-    const float bc = G.beta[16 * w + c];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sm.T[TT::off(16 * w + r, 16 * w + c)] = to_e<E>(x[r] * bc);
-  }
-}
-
-// Phase B part 2: off-diagonal blocks of R that wave W's block row of T
-// needs (wave W writes T_W0 .. T_W,W-1), by 16x16x16 products:
-// R_ij = -R_ii sum_{m=j}^{i-1} A_im R_mj.  Straight-line code per wave.
-template <typename E, int DK, int W>
-__device__ __forceinline__ void invert_offdiag_w(FwdSmem<E, DK> &sm, const Gates &G) {
-  using C = FwdCfg<E, DK>;
-  using TT = Tile<E, CH>;
-  const int l = lane_id(), n = l & 15, g = l >> 4;
-  const E *rr = &sm.Rr[W][0][0];
-  const E *rc = &sm.Rc[W][0][0];
-  constexpr int BS = 16 * C::LDR;
-  auto ablk = [&](int i, int k) {  // A_ik rows, fp32 -> E
-    f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.A[(16 * i + n) * C::LDA + 16 * k + 4 * g]);
-    F16<E> f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = to_e<E>(v[e]);
-    return f;
-  };
-  auto adiag = [&](int i) {  // rows of R_ii
-    return *reinterpret_cast<const F16<E> *>(rr + i * BS + n * C::LDR + 4 * g);
-  };
-  auto bdiag = [&](int j) {  // columns of R_jj (rows 4g..4g+3 of column n)
-    return *reinterpret_cast<const F16<E> *>(rc + j * BS + n * C::LDR + 4 * g);
-  };
-  auto put = [&](int i, int j, const f32x4 &R) {
-    const float bj = G.beta[16 * j + n];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.T[TT::off(16 * i + 4 * g + e, 16 * j + n)] = to_e<E>(R[e] * bj);
-  };
-  f32x4 y;
-  y = mma16(zero4(), ablk(1, 0), bdiag(0));
-  const f32x4 R10 = -mma16(zero4(), adiag(1), bfrag16<E>(y));
-  if constexpr (W == 1) {
-    put(1, 0, R10);
-  } else {
-    y = mma16(zero4(), ablk(2, 1), bdiag(1));
-    const f32x4 R21 = -mma16(zero4(), adiag(2), bfrag16<E>(y));
-    y = mma16(zero4(), ablk(2, 0), bdiag(0));
-    y = mma16(y, ablk(2, 1), bfrag16<E>(R10));
-    const f32x4 R20 = -mma16(zero4(), adiag(2), bfrag16<E>(y));
-    if constexpr (W == 2) {
-      put(2, 0, R20);
-      put(2, 1, R21);
-    } else {
-      y = mma16(zero4(), ablk(3, 2), bdiag(2));
-      const f32x4 R32 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
-      y = mma16(zero4(), ablk(3, 1), bdiag(1));
-      y = mma16(y, ablk(3, 2), bfrag16<E>(R21));
-      const f32x4 R31 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
-      y = mma16(zero4(), ablk(3, 0), bdiag(0));
-      y = mma16(y, ablk(3, 1), bfrag16<E>(R10));
-      y = mma16(y, ablk(3, 2), bfrag16<E>(R20));
-      const f32x4 R30 = -mma16(zero4(), adiag(3), bfrag16<E>(y));
-      put(3, 0, R30);
-      put(3, 1, R31);
-      put(3, 2, R32);
-    }
-  }
-}
-
-template <typename E, int DK>
-__device__ __forceinline__ void invert_offdiag(FwdSmem<E, DK> &sm, const Gates &G) {
-  const int w = wave_id();
-  if (w == 1) invert_offdiag_w<E, DK, 1>(sm, G);
-  else if (w == 2) invert_offdiag_w<E, DK, 2>(sm, G);
-  else if (w == 3) invert_offdiag_w<E, DK, 3>(sm, G);
-}
-
 template <typename E, int DK, bool GATED, bool STORE_STATES, bool WRITE_O>
 __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
   using C = FwdCfg<E, DK>;
@@ -299,11 +107,11 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
   const int col = dv0 + 16 * w + n;  // this lane's d_v column
   const size_t row_base = (size_t)si.b * p.T + si.t0;  // global row of the sequence start
 
-  // T and P: upper triangles stay zero
-  for (int i = threadIdx.x; i < CH * CH; i += NTHR) {
-    sm.T[i] = to_e<E>(0.f);
-    sm.P[i] = to_e<E>(0.f);
-  }
+  constexpr unsigned OUT = WRITE_O ? (OUT_P | OUT_T) : OUT_T;
+  PrepOut<E> po = {};
+  po.P = sm.P;
+  po.T = sm.T;
+  prep_zero<E, OUT>(po);  // upper triangles of T and P stay zero
 
   // state slice: lane (n, g) holds rows prow(mt, 4g + i) of column `col`
   f32x4 hacc[C::MTK];
@@ -379,8 +187,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[(size_t)prow(mt, 4 * g + i) * p.DV + col] = hacc[mt][i];
     }
-    build_kt<E, DK>(sm.KT, Kc);
-    phase_a<E, DK, GATED, WRITE_O>(sm, Kc, Qc, G);
+    transpose_tile<E, DK>(sm.KT, Kc);
+    prep_a<E, DK, OUT, GATED>(sm.ps, po, Kc, Qc, G);
     __syncthreads();
 
     // phase B: UT inverse overlapped with Y_K = K h, Y_Q = Q h
@@ -397,8 +205,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) yk[mt] = mma32(yk[mt], af[kb], hb[kb]);
     }
-    invert_diag<E, DK>(sm, G);
-    if (WRITE_O) {
+    prep_inv_diag<E, OUT>(sm.ps, po, G);
+    if constexpr (WRITE_O) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         F32<E> af[C::KB];
@@ -410,7 +218,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
       }
     }
     wave_lds_fence();
-    invert_offdiag<E, DK>(sm, G);
+    prep_inv_offdiag<E, OUT>(sm.ps, po, G);
     mfma_settle();  // Y_K, Y_Q and the inverse are read after the barrier
     __syncthreads();
 

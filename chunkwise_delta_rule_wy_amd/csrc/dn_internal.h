@@ -44,9 +44,44 @@ struct StepParams {
   int B, H, DV;
 };
 
+struct SeqInfo {
+  int b, t0, len;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const int32_t *cu, int n, int T) {
+  SeqInfo s;
+  if (cu) {
+    s.b = 0;
+    s.t0 = cu[n];
+    s.len = cu[n + 1] - s.t0;
+  } else {
+    s.b = n;
+    s.t0 = 0;
+    s.len = T;
+  }
+  return s;
+}
+
+// (pair, tile) of a workgroup.  Workgroups are dealt to the 8 XCDs round
+// robin; the d_v tiles of one (sequence, head) share K and Q, so they are
+// placed on one XCD (one L2).
+__device__ __forceinline__ void wg_coords(int x, int ntiles, int xcd_map, int &pair, int &tile) {
+  if (xcd_map) {
+    const int xcd = x & 7, slot = x >> 3;
+    pair = (slot / ntiles) * 8 + xcd;
+    tile = slot % ntiles;
+  } else {
+    pair = x / ntiles;
+    tile = x % ntiles;
+  }
+}
+
 size_t fwd_smem_bytes(int dtype, int DK);
+size_t fwd_ref_smem_bytes(int dtype, int DK);
 hipError_t launch_fwd(const FwdParams &p, int dtype, int DK, bool store_states, bool write_o,
                       hipStream_t stream);
+hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_states,
+                          bool write_o, hipStream_t stream);
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);

@@ -121,7 +121,11 @@ def test_fwd_deterministic_and_state_passing():
     for _ in range(3):
         o2, h2 = gpu_fwd(x)
         assert torch.equal(o1, o2) and torch.equal(h1, h2)
-    T1 = 128  # a chunk boundary: two segments equal one run up to rounding
+    # Split at a chunk boundary: two segments equal one run up to rounding.  The
+    # kernel carries the state scaled by a running product of decays and feeds
+    # it to the MFMA in bf16, so the two runs round it differently: they agree
+    # to the bf16 level, far inside the parity tolerance.
+    T1 = 128
     xa = {kk: (vv[:, :T1].contiguous() if kk in ("q", "k", "v", "beta", "g") else vv)
           for kk, vv in x.items()}
     oa, ha = gpu_fwd(xa)
@@ -129,7 +133,8 @@ def test_fwd_deterministic_and_state_passing():
           for kk, vv in x.items()}
     xb["h0"] = ha
     ob, hb = gpu_fwd(xb)
-    assert torch.equal(torch.cat([oa, ob], 1), o1) and torch.equal(hb, h1)
+    assert rel_l2(hb, h1) < 1e-2
+    assert rel_l2(torch.cat([oa, ob], 1), o1) < 1e-2
 
 
 def test_fwd_canary_no_out_of_bounds_writes():

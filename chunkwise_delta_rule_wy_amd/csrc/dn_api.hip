@@ -45,7 +45,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(const dn_shape *s, bool varlen) {
   BwdLayout L;
   const size_t nch = (size_t)max_chunks(s, varlen);
-  const size_t per = (size_t)s->H * s->Dk * s->Dv * sizeof(float);
+  const size_t per = (size_t)s->H * s->Dk * s->Dv * 2;  // bf16 states
   L.states = 0;
   L.dstates = align256(nch * per);
   L.table = L.dstates + align256(nch * per);
@@ -145,8 +145,8 @@ dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const vo
                                           (int)nchunks, stream);
     if (e != hipSuccess) return DN_EHIP;
   }
-  float *states = reinterpret_cast<float *>(ws + L.states);
-  float *dstates = reinterpret_cast<float *>(ws + L.dstates);
+  bf16 *states = reinterpret_cast<bf16 *>(ws + L.states);
+  bf16 *dstates = reinterpret_cast<bf16 *>(ws + L.dstates);
 
   // 1. forward sweep that stores every chunk-start state
   dn::FwdParams fp = {};

@@ -52,7 +52,7 @@ struct FwdSmem {
   Gates G[2];
 };
 
-template <typename E, int DK, bool GATED, bool STORE_STATES, bool WRITE_O>
+template <typename E, int DK, bool GATED, bool WRITE_O>
 __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
   using C = FwdCfg<E, DK>;
   using SM = FwdSmem<E, DK>;
@@ -147,14 +147,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
     if (c + 1 < nch) {
       if (C::NBUF == 2) issue_loads(c + 1, cur ^ 1);
       sc = load_scalars(c + 1);
-    }
-    if (STORE_STATES) {
-      const int cg = p.chunk_base ? p.chunk_base[n_seq] + c : n_seq * p.NC + c;
-      float *dst = p.states + ((size_t)cg * p.H + h) * DK * p.DV;
-#pragma unroll
-      for (int mt = 0; mt < C::MTK; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)prow(mt, 4 * g + i) * p.DV + col] = hacc[mt][i];
     }
     transpose_tile<E, DK>(sm.KT, Kc);
     prep_a<E, DK, OUT, GATED>(sm.ps, po, Kc, Qc, G);
@@ -262,11 +254,10 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename E, int DK, bool STORE_STATES, bool WRITE_O>
+template <typename E, int DK, bool WRITE_O>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
   const size_t smem = sizeof(FwdSmem<E, DK>);
-  auto kern = p.g ? fwd_kernel<E, DK, true, STORE_STATES, WRITE_O>
-                  : fwd_kernel<E, DK, false, STORE_STATES, WRITE_O>;
+  auto kern = p.g ? fwd_kernel<E, DK, true, WRITE_O> : fwd_kernel<E, DK, false, WRITE_O>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -277,25 +268,14 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
 }
 
 size_t fwd_ref_smem_bytes(int dtype, int DK) {
-  if (dtype == 1) return DK == 64 ? sizeof(FwdSmem<bf16, 64>) : sizeof(FwdSmem<bf16, 128>);
-  return DK == 64 ? sizeof(FwdSmem<float, 64>) : 0;  // fp32 needs d_k == 64 to fit LDS
+  return (dtype == 0 && DK == 64) ? sizeof(FwdSmem<float, 64>) : 0;  // fp32 needs d_k == 64 to fit LDS
 }
 
+// fp32 inputs, d_k = 64 (the state-storing variant is bf16 only)
 hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_states, bool write_o,
-                      hipStream_t stream) {
-#define DN_FWD_CASE(E, D)                                                       \
-  if (store_states)                                                             \
-    return write_o ? launch_fwd_t<E, D, true, true>(p, stream)                  \
-                   : launch_fwd_t<E, D, true, false>(p, stream);                \
-  return write_o ? launch_fwd_t<E, D, false, true>(p, stream)                   \
-                 : launch_fwd_t<E, D, false, false>(p, stream);
-  if (dtype == 1) {
-    if (DK == 64) { DN_FWD_CASE(bf16, 64) }
-    DN_FWD_CASE(bf16, 128)
-  }
-  if (DK == 64) { DN_FWD_CASE(float, 64) }
-  return hipErrorInvalidValue;
-#undef DN_FWD_CASE
+                          hipStream_t stream) {
+  if (dtype != 0 || DK != 64 || store_states) return hipErrorInvalidValue;
+  return write_o ? launch_fwd_t<float, 64, true>(p, stream) : launch_fwd_t<float, 64, false>(p, stream);
 }
 
 }  // namespace dn

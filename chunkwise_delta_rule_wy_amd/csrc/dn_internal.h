@@ -15,7 +15,7 @@ struct FwdParams {
   const int32_t *cu;          // device offsets, or null for fixed length
   void *o;                    // may be null when o is not written
   float *hT;                  // may be null
-  float *states;              // chunk-start states [chunk][H][DK][DV] (backward only)
+  bf16 *states;               // chunk-start states S = h^T, bf16 [chunk][H][DV][DK] (backward only)
   const int32_t *chunk_base;  // varlen: first global chunk of each sequence (backward only)
   int B, T, H, DV, N, NC;     // NC: chunks per sequence for fixed length
   int ntiles;                 // DV / 64
@@ -28,8 +28,8 @@ struct BwdParams {
   const int32_t *cu;
   const int32_t *chunk_base;  // varlen: first global chunk of each sequence
   const int32_t *chunk_seq;   // varlen: sequence of each global chunk
-  const float *states;        // chunk-start states
-  float *dstates;             // gradient w.r.t. each chunk's end state
+  const bf16 *states;         // chunk-start states S = h^T, bf16 [chunk][H][DV][DK]
+  bf16 *dstates;              // gradient w.r.t. each chunk's end state, same layout
   float *dq, *dk, *dv, *dbeta, *dg, *dh0;
   int B, T, H, DV, N, NC;
   int ntiles, xcd_map;
@@ -86,6 +86,6 @@ hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t strea
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream);
-size_t bwd_smem_bytes(int dtype, int DK);
+hipError_t launch_bwd_chunk(const BwdParams &p, int DK, hipStream_t stream);
 
 }  // namespace dn

@@ -95,9 +95,10 @@ def test_bwd_validation(lib):
 
 
 def test_bwd_workspace_covers_varlen_bound(lib):
-    # packed input: sum ceil(L/64) <= T/64 + n_seqs chunks of H*Dk*Dv fp32
+    # packed input: sum ceil(L/64) <= T/64 + n_seqs chunks; each chunk stores
+    # its state and state gradient, H*Dk*Dv bf16 each
     s1 = shape(B=1, T=1000, n_seqs=7)
-    per = 2 * 64 * 64 * 4
+    per = 2 * 64 * 64 * 2
     assert lib.dn_chunk_bwd_workspace(ctypes.byref(s1)) >= 2 * (1000 // 64 + 7) * per
 
 

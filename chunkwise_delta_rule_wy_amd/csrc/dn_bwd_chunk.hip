@@ -58,7 +58,7 @@ struct BLay {
   static constexpr int KQ = CH * RB;          // K, Q tile
   static constexpr int ST = CH * RB;          // S or dS tile (64 d_v rows)
   static constexpr int O_K = 0, O_Q = KQ;
-  using RS = Res<true>;
+  using RS = Res<MODE_CHUNK>;
   static constexpr int O_RES = 2 * KQ;         // prep results (the gate table holds beta too)
   static constexpr int O_BETA = O_RES + RS::BYTES;  // beta (0 past the end)
   static constexpr int O_X = O_BETA + 256;          // V'^T, Y^T; the prep scratch and g, beta before
@@ -96,7 +96,7 @@ __device__ __forceinline__ float sum4g(float x) {
 template <int DK, bool GATED>
 __global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
   using LY = BLay<DK>;
-  using RS = Res<true>;
+  using RS = Res<MODE_CHUNK>;
   constexpr int KB = LY::KB, MT = LY::MT, RB = LY::RB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const uint32_t sb = (uint32_t)(uintptr_t)(lds_ptr<unsigned char>)smem_raw;
@@ -243,10 +243,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
     const BwdKsw<DK> ksw{lb_frag};
     const uint32_t priv = sb + LY::O_X + w * PRIV_BYTES;
     const uint32_t kba = sb + LY::O_K, qba = sb + LY::O_Q, ga = sb + LY::O_XG, ba = sb + LY::O_XB;
-    if (w == 0) prep_chunk<DK, GATED, true, true, 0>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
-    else if (w == 1) prep_chunk<DK, GATED, true, true, 1>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
-    else if (w == 2) prep_chunk<DK, GATED, true, true, 2>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
-    else prep_chunk<DK, GATED, true, true, 3>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    if (w == 0) prep_chunk<DK, GATED, true, MODE_CHUNK, 0>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    else if (w == 1) prep_chunk<DK, GATED, true, MODE_CHUNK, 1>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    else if (w == 2) prep_chunk<DK, GATED, true, MODE_CHUNK, 2>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    else prep_chunk<DK, GATED, true, MODE_CHUNK, 3>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
   }
   __syncthreads();
 

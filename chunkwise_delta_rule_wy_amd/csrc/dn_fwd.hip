@@ -83,7 +83,7 @@ struct Lay {
   static constexpr int S_K = 0, S_Q = KQ, S_V = 2 * KQ, S_G = 2 * KQ + VT, S_BETA = S_G + 4 * CH;
   static constexpr int SLOT = S_BETA + 4 * CH;
   // prep results of one chunk
-  using RS = Res<false>;
+  using RS = Res<MODE_FWD>;
   static constexpr int O_P = RS::O_P, O_M = RS::O_M, O_TT = RS::O_TT, O_CG = RS::O_CG;
   static constexpr int OUTB = RS::BYTES;
   static constexpr int OUT_OFF = NBUF * SLOT;
@@ -363,13 +363,13 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
         const uint32_t priv = sbase + LY::PRIV_OFF + (uint32_t)v * LY::PRIV;
         const int L = min(CH, si.len - c * CH);
         const FwdKsw<DK> ksw{lb.frag};
-        if (v == 0) prep_chunk<DK, GATED, WRITE_O, false, 0>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
+        if (v == 0) prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 0>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
                                                          slot + LY::S_BETA, ob, priv, L, scale, ksw);
-        else if (v == 1) prep_chunk<DK, GATED, WRITE_O, false, 1>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
+        else if (v == 1) prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 1>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
                                                          slot + LY::S_BETA, ob, priv, L, scale, ksw);
-        else if (v == 2) prep_chunk<DK, GATED, WRITE_O, false, 2>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
+        else if (v == 2) prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 2>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
                                                          slot + LY::S_BETA, ob, priv, L, scale, ksw);
-        else prep_chunk<DK, GATED, WRITE_O, false, 3>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
+        else prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 3>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
                                                          slot + LY::S_BETA, ob, priv, L, scale, ksw);
       }
       // K, Q of chunk s + 2 (and everything older) land before the barrier;

@@ -86,6 +86,7 @@ hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t strea
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream);
+hipError_t launch_bwd_scan(const BwdParams &p, int DK, hipStream_t stream);
 hipError_t launch_bwd_chunk(const BwdParams &p, int DK, hipStream_t stream);
 
 }  // namespace dn

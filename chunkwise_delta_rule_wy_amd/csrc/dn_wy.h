@@ -88,15 +88,20 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float SCALE_MIN = 0x1p-30f;  // smallest forward state scale before a rescale
+constexpr float SCALE_MIN = 0x1p-30f;  // smallest state scale before a restart at 1
 
 // gate table of a chunk for the state-dependent work (fp32), byte offsets
-constexpr int CG_GS = 0;        // gamma_r s_c (backward: gamma_r)
-constexpr int CG_WS = 256;      // exp(b_63 - b_r) / s_{c+1} (backward: exp(b_63 - b_r))
-constexpr int CG_HSCALE = 512;  // forward: factor on h~ before the update (1: none)
-constexpr int CG_SC = 516;      // forward: s_c
-constexpr int CG_SNEXT = 520;   // forward: s_{c+1}
-constexpr int CG_BL = 512;      // backward: b_r log2(e)
+//   forward (state h = s_c h~):    GS = gamma_r s_c, WS = w_r / s_{c+1}
+//   reverse scan (dh = s_c dh~):   GS = gamma_r / s_c, WS = w_r s_{c+1}
+//   chunk gradients:               GS = gamma_r, WS = w_r, BL = b_r log2(e)
+// with w_r = exp(b_63 - b_r); HSCALE is the factor applied to the stored
+// state before the chunk's update when the scale restarts at 1 (1: none).
+constexpr int CG_GS = 0;
+constexpr int CG_WS = 256;
+constexpr int CG_HSCALE = 512;
+constexpr int CG_SC = 516;      // scale of the state entering the chunk's update
+constexpr int CG_SNEXT = 520;   // scale after it
+constexpr int CG_BL = 512;
 constexpr int CG_BYTES = 768;
 // a prep wave's own gate table (fp32), byte offsets
 constexpr int PG_BL = 0;      // b_r log2(e)
@@ -106,17 +111,21 @@ constexpr int PG_BYTES = 1280;
 constexpr int AT_BYTES = 1536;  // A_vv^T, fp32, 96-byte rows
 constexpr int PRIV_BYTES = AT_BYTES + PG_BYTES;
 
+// Which kernel a chunk preparation serves.
+enum : int { MODE_FWD = 0, MODE_CHUNK = 1, MODE_SCAN = 2 };
+
 // Results of the preparation of one chunk (byte offsets in a result buffer).
 //   forward:  P with rows 0..31 in 64-byte rows and rows 32..63 in 128-byte
 //             rows; -M_ij (i > j) in six 16 x 16 blocks; T_ii^T.
-//   backward: P^T, 64 x 64 in 128-byte rows; -M_ij (i > j) in six blocks and
-//             M_ii^T in four more; R_ii^T.
-template <bool BWD>
+//   chunk gradients: P^T, 64 x 64 in 128-byte rows; -M_ij (i > j) in six
+//             blocks and M_ii^T in four more; R_ii^T.
+//   reverse scan: P^T; -M_ij (i > j); R_ii^T.
+template <int MODE>
 struct Res {
   static constexpr int O_P = 0;
-  static constexpr int P_BYTES = BWD ? 8192 : 6144;
+  static constexpr int P_BYTES = MODE == MODE_FWD ? 6144 : 8192;
   static constexpr int O_M = P_BYTES;
-  static constexpr int O_TT = O_M + (BWD ? 10 : 6) * 512;
+  static constexpr int O_TT = O_M + (MODE == MODE_CHUNK ? 10 : 6) * 512;
   static constexpr int O_CG = O_TT + 2048;
   static constexpr int BYTES = O_CG + CG_BYTES;
   static_assert(BYTES % 256 == 0, "alignment");
@@ -207,15 +216,17 @@ using I3 = std::integral_constant<int, 3>;
 // M = strictLower((K K^T) * Gamma), P = (Q K^T) * Gamma (lower, with the
 // diagonal), A = diag(beta) M.  The forward variant stores T_vv =
 // (I + A_vv)^-1 diag(beta) (transposed) and the gate table with the state
-// scale carried in `scale` by wave 0; the backward variant stores R_vv =
-// (I + A_vv)^-1 (transposed), P^T instead of P, M_vv^T and the plain gate
-// table.  kbase, qbase: K and Q tiles (K-tile swizzle KSW); gaddr, baddr:
+// scale carried in `scale` by wave 0; the backward variants store R_vv =
+// (I + A_vv)^-1 (transposed) and P^T instead of P, the chunk-gradient one also
+// M_vv^T and the plain gate table, the scan one the gate table of the scaled
+// state gradient.  kbase, qbase: K and Q tiles (K-tile swizzle KSW); gaddr, baddr:
 // g and beta of the chunk's rows (fp32, LDS); rows >= L are padding.
-template <int DK, bool GATED, bool WRITE_P, bool BWD, int PW, typename KSW>
+template <int DK, bool GATED, bool WRITE_P, int MODE, int PW, typename KSW>
 __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint32_t qbase, uint32_t gaddr,
                                            uint32_t baddr, uint32_t ob, uint32_t priv, int L, float &scale,
                                            KSW ksw) {
-  using RS = Res<BWD>;
+  using RS = Res<MODE>;
+  constexpr bool BWD = MODE != MODE_FWD;
   constexpr int KB = DK / 32;
   const int l = lane_id(), n = l & 15, g = l >> 4;
   const uint32_t pg = priv + AT_BYTES;
@@ -232,17 +243,24 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     st<float>(pg + PG_KAP + 512 + 4 * l, fexp2(b48 - b));
     if constexpr (PW == 0) {
       const float b63 = lane_val(b, 63);
-      if constexpr (BWD) {
+      if constexpr (MODE == MODE_CHUNK) {
         st<float>(ob + RS::O_CG + CG_GS + 4 * l, fexp2(b));
         st<float>(ob + RS::O_CG + CG_WS + 4 * l, fexp2(b63 - b));
         st<float>(ob + RS::O_CG + CG_BL + 4 * l, b);
       } else {
+        // the state (forward) or state gradient (scan) of scale sc is multiplied by
+        // gamma_63 in this chunk's update: t is the next scale unless it restarts
         const float sc = scale;
         const float t = sc * fexp2(b63);
         const bool resc = !(t >= SCALE_MIN);
         const float inv = resc ? 1.f : 1.f / t;
-        st<float>(ob + RS::O_CG + CG_GS + 4 * l, fexp2(b) * sc);
-        st<float>(ob + RS::O_CG + CG_WS + 4 * l, fexp2(b63 - b) * inv);
+        if constexpr (MODE == MODE_FWD) {
+          st<float>(ob + RS::O_CG + CG_GS + 4 * l, fexp2(b) * sc);
+          st<float>(ob + RS::O_CG + CG_WS + 4 * l, fexp2(b63 - b) * inv);
+        } else {
+          st<float>(ob + RS::O_CG + CG_GS + 4 * l, fexp2(b) * inv);
+          st<float>(ob + RS::O_CG + CG_WS + 4 * l, fexp2(b63 - b) * sc);
+        }
         if (l == 0) {
           st<float>(ob + RS::O_CG + CG_HSCALE, resc ? t : 1.f);
           st<float>(ob + RS::O_CG + CG_SC, sc);
@@ -284,7 +302,7 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
       a[e] = keep ? be[e] * mv[e] : 0.f;
     }
     st<f32x4>(priv + 96 * n + 16 * g, a);
-    if constexpr (BWD) st<bf16x4>(ob + RS::O_M + 512 * (6 + PW) + lb.m, cvt4(mv));  // M_vv^T row n
+    if constexpr (MODE == MODE_CHUNK) st<bf16x4>(ob + RS::O_M + 512 * (6 + PW) + lb.m, cvt4(mv));  // M_vv^T row n
   }
 
   // Block (TI, TJ) of -M below the diagonal: lane (n, g) holds k_r . k_j with

@@ -332,6 +332,8 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
       hs[mt][i] = (chain && p.h0) ? p.h0[st_base + (size_t)r * DV + col] : 0.f;
     }
   float scale = 1.f;  // prep wave 0: state scale s_c of the next chunk it prepares
+  // global chunk index of the sequence's first chunk (state slots)
+  const int cg0 = STORE_STATES ? (p.chunk_base ? p.chunk_base[n_seq] : n_seq * p.NC) : 0;
 
   if (!chain) {
     if (nch > 0) issue(0);
@@ -347,10 +349,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
         const uint32_t ob = sbase + LY::OUT_OFF + (uint32_t)(s & 1) * LY::OUTB;
         const int L = min(CH, si.len - s * CH);
         bf16 *sdst = nullptr;
-        if (STORE_STATES) {
-          const int cg = p.chunk_base ? p.chunk_base[n_seq] + s : n_seq * p.NC + s;
-          sdst = p.states + ((size_t)cg * H + h) * (size_t)DV * DK;
-        }
+        if (STORE_STATES) sdst = p.states + ((size_t)(cg0 + s) * H + h) * (size_t)DV * DK;
         chain_chunk<DK, GATED, STORE_STATES, WRITE_O>(p, lb, hs, slot, ob, L, row_base + (size_t)s * CH, h,
                                                       col, sdst);
       }

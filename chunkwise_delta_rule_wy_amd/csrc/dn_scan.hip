@@ -293,6 +293,8 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
       hs[mt][i] = (chain && p.dhT) ? p.dhT[st_base + (size_t)r * DV + col] : 0.f;
     }
   float scale = 1.f;  // prep wave 0: scale of dh entering the next chunk it prepares
+  // global chunk index of the sequence's first chunk (state slots)
+  const int cg0 = p.chunk_base ? p.chunk_base[n_seq] : n_seq * p.NC;
 
   if (!chain) {
     if (nch > 0) issue(0);
@@ -306,8 +308,7 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
       if (s >= 0) {
         const int c = chunk_of(s);
         const uint32_t ob = sbase + LY::OUT_OFF + (uint32_t)(s & 1) * LY::OUTB;
-        const int cg = p.chunk_base ? p.chunk_base[n_seq] + c : n_seq * p.NC + c;
-        bf16 *dst = p.dstates + (((size_t)cg * H + h) * DV + col) * DK + 8 * g;
+        bf16 *dst = p.dstates + (((size_t)(cg0 + c) * H + h) * DV + col) * DK + 8 * g;
         chain_chunk<DK, GATED>(lb, hs, slot_of(s), ob, dtr, dpr, dst);
       }
     } else {

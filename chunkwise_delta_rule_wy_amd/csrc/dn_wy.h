@@ -42,12 +42,24 @@ __device__ __forceinline__ void st(uint32_t a, const T &v) {
 __device__ __forceinline__ bf16x4 ld_tr(uint32_t a) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr<s16x4>)(size_t)(a)));
 }
-// direct global -> LDS loads of 16 or 4 bytes per lane; lane l writes dst + 16 l (or 4 l)
+// Direct global -> LDS loads of 16 or 4 bytes per lane; lane l writes dst + 16 l
+// (or 4 l), dst wave-uniform (it goes to M0).  They are issued from inline
+// assembly on purpose: the compiler's wait insertion treats every transposed
+// LDS read (ds_read_b64_tr_b16) after a direct load as dependent on it and
+// waits for all outstanding vector memory operations, which would drain the
+// prefetch ring on every step.  The kernels order these loads themselves with
+// wait_vm<N> and barriers; the compiler's own waits for its loads and stores
+// only become more conservative, since it does not count these.  The s_nop
+// covers the one wait state an LDS DMA needs after M0 is written by SALU.
 __device__ __forceinline__ void dma16(const void *src, uint32_t dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr<void>)(size_t)dst, 16, 0, 0);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
 }
 __device__ __forceinline__ void dma4(const void *src, uint32_t dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr<void>)(size_t)dst, 4, 0, 0);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+}
+// the same with a wave-uniform base address and a 32-bit per-lane byte offset
+__device__ __forceinline__ void dma16s(const void *base, uint32_t voff, uint32_t dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(dst) : "memory");
 }
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }

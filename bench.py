@@ -8,10 +8,12 @@ B=4 T=4096 H=16 dk=128 dv=256) that is the chunkwise forward pass plus the
 chunkwise backward pass (dq, dk, dv, dbeta, dg, dh0).  Workloads 2, 3 and 5
 are forward-only; "dec" is one decode step at batch 256, H=32, d=128.
 
-Prints one JSON line: tokens/s over the timed steps, the roofline position of
-the forward kernel (timed live with HIP events on the launch stream), and the
-fp64 oracle's throughput on a bounded sample of the same workload on the host
-cores.
+Prints one JSON line: tokens/s and algorithmic TFLOP/s (with the fraction of
+the bf16 MFMA peak) over the timed steps, every kernel's device time from HIP
+events recorded on the launch stream inside the timed steps, the roofline
+position of the dominant kernel (the chunk-gradient kernel of the backward
+pass; the forward kernel for forward-only workloads), and the fp64 oracle's
+throughput on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -42,6 +44,29 @@ def workload_bytes(sh, backward: bool) -> float:
                 + 2 * sh.Dk * 4 + sh.Dv * 4 + 4 * (2 if sh.gated else 1))      # dq dk dv dbeta dg
     bwd += st * (1 + 1 + 1)                                                    # h0 dhT dh0
     return float(fwd + bwd)
+
+
+def chunk_grad_bytes(sh) -> float:
+    """Algorithmic HBM bytes of one launch of the chunk-gradient kernel: per
+    (chunk, head) it reads q, k, v, dO, beta, g and the two bf16 chunk states
+    (h and dh, d_k x d_v each) and writes dq, dk, dv, dbeta, dg in fp32."""
+    es = 2 if str(sh.dtype).endswith("bfloat16") else 4
+    th = sh.B * sh.T * sh.H
+    lengths = sh.lengths if sh.lengths is not None else [sh.T] * sh.B
+    chunk_heads = sum((L + 63) // 64 for L in lengths) * sh.H
+    per_tok = (2 * sh.Dk * es + 2 * sh.Dv * es + 4 * (2 if sh.gated else 1)
+               + 2 * sh.Dk * 4 + sh.Dv * 4 + 4 * (2 if sh.gated else 1))
+    return float(th * per_tok + chunk_heads * 2 * sh.Dk * sh.Dv * 2)
+
+
+def bwd_flops(sh) -> float:
+    """Algorithmic flops of the backward pass without the recompute, per
+    token-head (MACs): 6 dk dv for the state products, (C+1)/2 (5 dk + 4 dv)
+    for the causal intra-chunk products, (C-1)/2 2 dk for the strict ones and
+    2 C^2/3 for the two triangular substitutions."""
+    C, dk, dv = 64, sh.Dk, sh.Dv
+    mac = 6 * dk * dv + (C + 1) / 2 * (5 * dk + 4 * dv) + (C - 1) / 2 * 2 * dk + 2 * C * C / 3
+    return 2.0 * mac * sh.B * sh.T * sh.H
 
 
 def fwd_flops(sh) -> float:
@@ -89,44 +114,53 @@ def main():
         ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv, sh.n_seqs,
                                                 sh.dtype), dtype=torch.uint8, device=dev)
 
-    def step():
+    # every timed step records HIP events on the stream the kernels run on
+    # (torch's current stream, which the binding hands to the library)
+    stream = torch.cuda.current_stream(dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    nev = max(args.steps, 1)
+    fev = [(mk(), mk()) for _ in range(nev)]
+    bev = [[mk() for _ in range(4)] for _ in range(nev)] if backward else None
+
+    def step(i=None):
+        if i is not None:
+            fev[i][0].record(stream)
         o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+        if i is not None:
+            fev[i][1].record(stream)
         if backward:
             dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
-                         d["cu_seqlens"], workspace=ws)
+                         d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None)
         return o
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / max(args.steps, 1)
     tokens = sh.B * sh.T
     value = tokens / (ms_per_step * 1e-3)
 
-    # the forward kernel alone, timed with HIP events on its launch stream
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    nf = max(args.steps, 5)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(nf):
-        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
-    ev1.record(stream)
-    ev1.synchronize()
-    fwd_us = ev0.elapsed_time(ev1) * 1e3 / nf
-    fbytes = workload_bytes(sh, False)
-    achieved = fbytes / (fwd_us * 1e-6) / 1e9
+    # per-kernel device time, averaged over the timed steps
+    avg = lambda pairs: sum(a.elapsed_time(b) for a, b in pairs) * 1e3 / len(pairs)
+    stage_us = {"fwd": avg(fev[:args.steps])}
+    if backward:
+        for j, name in enumerate(("recompute", "state_grad_scan", "chunk_grad")):
+            stage_us[name] = avg([(e[j], e[j + 1]) for e in bev[:args.steps]])
+    flops = fwd_flops(sh) + (bwd_flops(sh) if backward else 0.0)
+    if backward:
+        kname, kus, kbytes = "dn::bwd_chunk_kernel", stage_us["chunk_grad"], chunk_grad_bytes(sh)
+    else:
+        kname, kus, kbytes = "dn::fwd_bf16_kernel", stage_us["fwd"], workload_bytes(sh, False)
+    achieved = kbytes / (kus * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "dn::fwd_kernel", "kernel_us": round(fwd_us, 2),
-                "bytes_per_launch": fbytes,
-                "tflops": round(fwd_flops(sh) / (fwd_us * 1e-6) / 1e12, 2)}
+                "kernel": kname, "kernel_us": round(kus, 2), "bytes_per_launch": kbytes}
+    step_tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     out = {
         "metric": "tokens/s & TFLOP/s (fraction of MFMA peak), gated delta-rule fwd+bwd",
@@ -145,7 +179,10 @@ def main():
                    "Dk": sh.Dk, "Dv": sh.Dv, "chunk": 64, "passes": "fwd+bwd" if backward else "fwd",
                    "n_seqs": sh.n_seqs},
         "roofline": roofline,
+        "tflops": round(step_tflops, 2),
+        "mfma_frac": round(step_tflops / MFMA_BF16_PEAK_TFS, 4),
         "step_gbs": round(workload_bytes(sh, backward) / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernel_us": {k: round(v, 2) for k, v in stage_us.items()},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds)

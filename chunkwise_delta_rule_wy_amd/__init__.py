@@ -68,6 +68,8 @@ def load_library():
     lib.dn_chunk_fwd.restype = ctypes.c_int
     lib.dn_chunk_bwd.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P, ctypes.c_size_t, P]
     lib.dn_chunk_bwd.restype = ctypes.c_int
+    lib.dn_chunk_bwd_events.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
+    lib.dn_chunk_bwd_events.restype = ctypes.c_int
     lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
     lib.dn_recurrent_step.restype = ctypes.c_int
     _lib = lib
@@ -148,12 +150,15 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_stat
 
 
 def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 64,
-              workspace: Optional[torch.Tensor] = None):
+              workspace: Optional[torch.Tensor] = None, events=None):
     """Backward pass of ``<dO, o> + <dhT, hT>``.
 
     Returns a dict of float32 gradients dq, dk, dv, dbeta, dg (None without a
     gate) and dh0.  ``workspace`` (uint8, at least ``bwd_workspace_bytes``)
-    may be passed to avoid an allocation per call.
+    may be passed to avoid an allocation per call.  ``events``: four
+    ``torch.cuda.Event(enable_timing=True)`` that the library records before
+    its first kernel and after the recompute, the state-gradient sweep and the
+    chunk-gradient kernel (``dn_chunk_bwd_events``).
     """
     lib = load_library()
     s, N = _shape(q, v, cu_seqlens, chunk)
@@ -178,10 +183,18 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     wsb = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    _check("dn_chunk_bwd", lib.dn_chunk_bwd(
+    ev = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events: four torch.cuda.Event objects expected")
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the event on its first record
+                e.record(torch.cuda.current_stream(dev))
+        ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    _check("dn_chunk_bwd", lib.dn_chunk_bwd_events(
         ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
         _ptr(cu_seqlens), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),
-        _ptr(dg), _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(dev)))
+        _ptr(dg), _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(dev), ev))
     return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dh0=dh0)
 
 

@@ -121,6 +121,16 @@ dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const vo
                        const int32_t *cu_seqlens, const void *dO, const float *dhT, float *dq,
                        float *dk, float *dv, float *dbeta, float *dg, float *dh0, void *workspace,
                        size_t workspace_bytes, hipStream_t stream) {
+  return dn_chunk_bwd_events(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq, dk, dv, dbeta, dg, dh0,
+                             workspace, workspace_bytes, stream, nullptr);
+}
+
+dn_status dn_chunk_bwd_events(const dn_shape *s, const void *q, const void *k, const void *v,
+                              const float *beta, const float *g, const float *h0,
+                              const int32_t *cu_seqlens, const void *dO, const float *dhT, float *dq,
+                              float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream,
+                              hipEvent_t *events) {
   dn_status st = check_shape(s, cu_seqlens);
   if (st != DN_OK) return st;
   if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
@@ -147,6 +157,7 @@ dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const vo
   }
   bf16 *states = reinterpret_cast<bf16 *>(ws + L.states);
   bf16 *dstates = reinterpret_cast<bf16 *>(ws + L.dstates);
+  if (events && hipEventRecord(events[0], stream) != hipSuccess) return DN_EHIP;
 
   // 1. forward sweep that stores every chunk-start state
   dn::FwdParams fp = {};
@@ -171,6 +182,7 @@ dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const vo
   fp.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
   hipError_t e = dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
   if (e != hipSuccess) return DN_EHIP;
+  if (events && hipEventRecord(events[1], stream) != hipSuccess) return DN_EHIP;
 
   // 2. reverse sweep for the state gradients, 3. chunk-parallel token gradients
   dn::BwdParams bp = {};
@@ -201,7 +213,8 @@ dn_status dn_chunk_bwd(const dn_shape *s, const void *q, const void *k, const vo
   bp.ntiles = s->Dv / 64;
   bp.xcd_map = fp.xcd_map;
   bp.total_chunks = (int)nchunks;
-  return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream));
+  return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream, events ? events[2] : nullptr,
+                                 events ? events[3] : nullptr));
 }
 
 dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,

@@ -66,11 +66,16 @@ hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream, hipEvent_t ev_scan,
+                      hipEvent_t ev_chunk) {
   if (dtype != 1) return hipErrorInvalidValue;  // bf16 only
   hipError_t e = launch_bwd_scan(p, DK, stream);
   if (e != hipSuccess) return e;
-  return launch_bwd_chunk(p, DK, stream);
+  if (ev_scan && (e = hipEventRecord(ev_scan, stream)) != hipSuccess) return e;
+  e = launch_bwd_chunk(p, DK, stream);
+  if (e != hipSuccess) return e;
+  if (ev_chunk) e = hipEventRecord(ev_chunk, stream);
+  return e;
 }
 
 }  // namespace dn

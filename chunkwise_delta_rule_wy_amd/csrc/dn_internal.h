@@ -85,7 +85,10 @@ hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_stat
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream);
+// ev_scan / ev_chunk (may be null) are recorded on `stream` after the scan and
+// after the chunk-gradient kernel
+hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream, hipEvent_t ev_scan = nullptr,
+                      hipEvent_t ev_chunk = nullptr);
 hipError_t launch_bwd_scan(const BwdParams &p, int DK, hipStream_t stream);
 hipError_t launch_bwd_chunk(const BwdParams &p, int DK, hipStream_t stream);
 

@@ -111,6 +111,25 @@ dn_status dn_chunk_bwd(const dn_shape *s,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dn_chunk_bwd with stage timing: the same operation, arguments and errors,
+ * and in addition it records events[0] on `stream` before its first kernel,
+ * events[1] after the state recompute, events[2] after the reverse
+ * state-gradient sweep and events[3] after the chunk-gradient kernel (whose
+ * launch follows the sweep directly), so that hipEventElapsedTime on
+ * consecutive pairs gives each stage's device time.  The four events are
+ * created (with timing enabled) and owned by the caller; events == NULL is
+ * dn_chunk_bwd.  A failed record returns DN_EHIP.
+ */
+dn_status dn_chunk_bwd_events(const dn_shape *s,
+                              const void *q, const void *k, const void *v,
+                              const float *beta, const float *g, const float *h0,
+                              const int32_t *cu_seqlens,
+                              const void *dO, const float *dhT,
+                              float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream,
+                              hipEvent_t *events);
+
+/*
  * One recurrent (decode) step for B x H independent states: the token update
  * above applied once (Gated DeltaNet review thread, General Response 2: the
  * recurrent step is memory-bound and its cost is set by the state size).

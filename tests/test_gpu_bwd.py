@@ -91,6 +91,23 @@ def test_bwd_deterministic():
             assert torch.equal(a[name], b[name]), name
 
 
+def test_bwd_stage_events():
+    """dn_chunk_bwd_events gives dn_chunk_bwd's gradients bit for bit and
+    records its four events in stream order."""
+    sh = Shape(1, 200, 2, 128, 256, torch.bfloat16, True, True, backward=True)
+    x = make_inputs(sh, seed=39)
+    a = gpu_bwd(x)
+    d = to_dev(x)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    gr = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
+                      events=ev)
+    ev[3].synchronize()
+    for name in NAMES:
+        assert torch.equal(a[name], gr[name].cpu()), name
+    for i in range(3):
+        assert ev[i].elapsed_time(ev[i + 1]) > 0.0
+
+
 def test_autograd_wrapper_matches_entry_points():
     sh = Shape(1, 100, 2, 128, 128, torch.bfloat16, True, True, backward=True)
     x = to_dev(make_inputs(sh, seed=37))

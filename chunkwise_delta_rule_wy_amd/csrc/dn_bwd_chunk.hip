@@ -1,5 +1,5 @@
 // Chunk-parallel gradients of the chunkwise (gated) delta rule for gfx950,
-// bf16 inputs: one workgroup (4 waves) per (chunk, head) with all d_v
+// bf16 inputs: one workgroup (8 waves) per (chunk, head) with all d_v
 // columns, so that products contracting over d_v need no cross-workgroup sums.
 //
 // Inputs per chunk: K, Q, V, dO, beta, g, the state entering the chunk h and
@@ -31,11 +31,26 @@
 // over Sequence Length" (page 1, answer Q2) with the UT form of the Gated
 // DeltaNet review thread (review 2).
 //
-// Per 64-wide d_v tile, wave w first owns columns 16w .. 16w + 15 (X, V',
-// dV', Y, dv) and hands V'^T and Y^T to the others through LDS; then it owns
-// token rows 16w .. 16w + 15 of the products contracting over the tile's d_v
-// columns (dP, dA, dO h^T, Y h^T, V' dh^T), accumulated in registers over the
-// tiles.  The tiles' V, dO, S and dS arrive by direct loads, one tile ahead.
+// Organisation.  d_v is walked in 32-column tiles through a two-stage
+// pipeline; in step s
+//   column waves 0..3  take tile s.  Wave 2c ("F") owns tile columns
+//                      16c .. 16c + 15 for X = V - gamma K h and the forward
+//                      substitution (V'); wave 2c + 1 ("B") the same columns
+//                      for dV' = w K dh + P^T dO, the backward substitution
+//                      (Y), dX and dv.  They hand V'^T and Y^T to the row
+//                      waves through one of two LDS buffers.
+//   row waves 4..7     take tile s - 1: each owns 16 token rows of the
+//                      products contracting over the tile's columns (dP, dA,
+//                      dO h^T, Y h^T, V' dh^T), accumulated in registers over
+//                      all tiles, and issues the direct loads of tile s + 2.
+// Wave w and wave w + 4 share a SIMD, so a column wave's dependent chain of
+// small MFMAs and a row wave's stream of independent ones fill each other's
+// stalls.  Each role runs its own loop with one barrier per step; the roles
+// keep their own registers (a wave's state never holds another role's).
+// Tiles arrive two steps ahead in a ring of four LDS buffers.  After the last
+// step the row waves form dPG = dP * Gamma and F and write them transposed;
+// then the row waves compute dq and their share of dk, the column waves
+// dPG^T Q + F^T K, and wave 0 dbeta and dg.
 #include "dn_wy.h"
 
 namespace dn {
@@ -43,34 +58,47 @@ namespace {
 
 using namespace wy;
 
-// swizzles of this kernel's tiles (linear in the row bits, bit 0 never set)
+constexpr int BW_THREADS = 512;  // eight waves
+constexpr int TC = 32;           // d_v columns per tile
+
+// swizzles of this kernel's tiles (linear in the row bits)
 template <int DK>
 __device__ __forceinline__ int swz_s(int r) {  // K, Q, S, dS (rows of 2 d_k bytes)
   if constexpr (DK == 128) return ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3);
   else return (r & 2) | (((r >> 3) & 1) << 2);
 }
-__device__ __forceinline__ int swz_d(int r) { return (r & 2) | (((r >> 3) & 1) << 2); }          // dO
-__device__ __forceinline__ int swz_x(int r) { return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2); }  // V'^T, Y^T
+__device__ __forceinline__ int swz_v32(int r) { return ((r >> 2) & 1) << 1; }  // V tile, 64-byte rows
+__device__ __forceinline__ int swz_d32(int r) { return ((r >> 3) & 1) << 1; }  // dO tile, 64-byte rows
+__device__ __forceinline__ int swz_x(int r) { return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2); }
 
 template <int DK>
 struct BLay {
   static constexpr int RB = 2 * DK, KB = DK / 32, MT = DK / 16;
-  static constexpr int KQ = CH * RB;          // K, Q tile
-  static constexpr int ST = CH * RB;          // S or dS tile (64 d_v rows)
+  static constexpr int KQ = CH * RB;           // K, Q tile
   static constexpr int O_K = 0, O_Q = KQ;
   using RS = Res<MODE_CHUNK>;
   static constexpr int O_RES = 2 * KQ;         // prep results (the gate table holds beta too)
   static constexpr int O_BETA = O_RES + RS::BYTES;  // beta (0 past the end)
-  static constexpr int O_X = O_BETA + 256;          // V'^T, Y^T; the prep scratch and g, beta before
-  static constexpr int X_BYTES = 16384;
+  static constexpr int O_X = O_BETA + 256;     // two hand-over buffers; the prep scratch and g, beta before
+  static constexpr int XB = 8192;              // V'^T (32 x 64 bf16) then Y^T
   static constexpr int O_XG = O_X + 4 * PRIV_BYTES;  // direct-load targets of g and beta
   static constexpr int O_XB = O_XG + 256;
-  static constexpr int O_T = O_X + X_BYTES;    // two tile buffers: V, dO, S, dS
-  static constexpr int T_V = 0, T_DO = 8192, T_S = 16384, T_DS = 16384 + ST;
-  static constexpr int TB = 16384 + 2 * ST;
-  static constexpr int TOTAL = O_T + 2 * TB;
-  static constexpr int DMA_KQ = KQ / 4096, DMA_S = ST / 4096;  // direct loads per wave
-  static_assert(O_XB + 256 <= O_X + X_BYTES, "scratch fits");
+  static constexpr int O_T = O_X + 2 * XB;     // ring of tile buffers: V, dO (64 x 32), S, dS (32 x d_k)
+  static constexpr int ST = TC * RB;
+  static constexpr int T_V = 0, T_DO = 4096, T_S = 8192, T_DS = 8192 + ST;
+  static constexpr int TB = 8192 + 2 * ST;
+  static constexpr int NBUF = 4;
+  static constexpr int TOTAL = O_T + NBUF * TB;
+  static constexpr int DMA_T = TB / 16 / 256;   // direct loads per row-wave lane per tile
+  static constexpr int DMA_KQ = KQ / 16 / 512;  // per lane and matrix
+  static constexpr int DMA_S = ST / 16 / 256;   // of S (and of dS) per row-wave lane
+  // final phase, in the tile ring
+  static constexpr int O_FIN = O_T;             // dPG^T, F^T (P^T layout)
+  static constexpr int O_RED = O_T + 16384;     // reductions
+  static constexpr int O_DKX = O_T + 20480;     // column waves' share of dk, fp32
+  static_assert(O_XB + 256 <= O_X + 2 * XB, "scratch fits");
+  static_assert(O_DKX + 4 * MT * 64 * 16 <= TOTAL, "final phase fits");
+  static_assert(DMA_T == 2 + 2 * DMA_S, "tile = V, dO, S, dS");
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -94,7 +122,7 @@ __device__ __forceinline__ float sum4g(float x) {
 }
 
 template <int DK, bool GATED>
-__global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
+__global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   using LY = BLay<DK>;
   using RS = Res<MODE_CHUNK>;
   constexpr int KB = LY::KB, MT = LY::MT, RB = LY::RB;
@@ -115,43 +143,27 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
   const SeqInfo si = seq_info(p.cu, n_seq, p.T);
   if (c * CH >= si.len) return;
   const int L = min(CH, si.len - c * CH);
-  const int H = p.H, DV = p.DV, ntiles = p.ntiles;
+  const bool full = L == CH;
+  const int H = p.H, DV = p.DV, ntiles = p.DV / TC;
   const size_t row0 = (size_t)si.b * p.T + si.t0 + (size_t)c * CH;  // global row of the chunk start
-  const int w = wave_id(), l = lane_id(), n = l & 15, g = l >> 4, e4 = (l >> 2) & 3, q4 = l & 3;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = lane_id(), n = l & 15, g = l >> 4, e4 = (l >> 2) & 3, q4 = l & 3;
 
   // ---- lane bases
   const int sn = swz_s<DK>(n);
-  const uint32_t lb_frag = n * RB + 16 * (g ^ (sn & 3)) + 64 * (sn >> 2);  // K/Q/S frag
-  uint32_t lb_str[2];  // S-like transposed reads, rows 32kb + 8g + 4hh + e, columns 16mt + 4q
+  const uint32_t lb_frag = n * RB + 16 * (g ^ (sn & 3)) + 64 * (sn >> 2);  // K/Q/S frag, row n
+  uint32_t lb_str[2];  // S-like transposed reads, rows 8g + 4hh + e, columns 16mt + 4q
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int r = 8 * g + 4 * hh + e4, s = swz_s<DK>(r);
     lb_str[hh] = r * RB + 8 * q4 + 32 * (s >> 1);
   }
-  uint32_t lb_rtr;  // rows 16w + 4g + e, columns 16mt + 4q (K and Q reads of the db terms)
-  {
-    const int r = 4 * g + e4, s = swz_s<DK>(r);
-    lb_rtr = (16 * w + r) * RB + 8 * q4 + 32 * (s >> 1);
-  }
-  uint32_t lb_dtr[2];  // dO transposed reads, rows 32kb + 8g + 4hh + e, columns 16w + 4q
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int r = 8 * g + 4 * hh + e4, s = swz_d(r);
-    lb_dtr[hh] = r * 128 + 16 * ((2 * w + (q4 >> 1)) ^ s) + 8 * (q4 & 1);
-  }
-  const int sdn = swz_d(n);
-  const uint32_t lb_dfrag = (16 * w + n) * 128 + 16 * (g ^ (sdn & 3)) + 64 * (sdn >> 2);  // dO frag, row 16w + n
-  uint32_t lb_vtr;  // V transposed reads, rows 16t + 4g + e, columns 16w + 4q
-  {
-    const int r = 4 * g + e4;
-    lb_vtr = r * 128 + 16 * ((2 * w + (q4 >> 1)) ^ swz_v(r)) + 8 * (q4 & 1);
-  }
-  uint32_t lb_xw;  // V'^T / Y^T write: row 16w + n, columns 16i + 4g: 16w*128 + (lb_xw ^ 32 i)
+  uint32_t lb_xw;  // V'^T / Y^T row n, tokens 16i + 4g: lb_xw ^ 32 i
   {
     const int s = swz_x(n);
     lb_xw = n * 128 + 32 * (s >> 1) + 16 * ((g >> 1) ^ (s & 1)) + 8 * (g & 1);
   }
-  uint32_t lb_xtr[2];  // V'^T / Y^T transposed reads: rows 32kb + 8g + 4hh + e, columns 16jt + 4q
+  uint32_t lb_xtr[2];  // V'^T / Y^T transposed reads: rows 8g + 4hh + e, tokens 16jt + 4q
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int r = 8 * g + 4 * hh + e4, s = swz_x(r);
@@ -164,27 +176,29 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
   lb.m = lb_m;
   lb.btr = lb_btr;
 
+  const uint32_t ob = sb + LY::O_RES, cgt = ob + RS::O_CG;
+  auto tbuf = [&](int j) { return sb + LY::O_T + (uint32_t)(j % LY::NBUF) * LY::TB; };
+  auto xbuf = [&](int j) { return sb + LY::O_X + (uint32_t)(j & 1) * LY::XB; };
+  auto gam4 = [&](int i) { return GATED ? ld<f32x4>(cgt + CG_GS + 4 * (16 * i + 4 * g)) : (f32x4){1.f, 1.f, 1.f, 1.f}; };
+  auto w4 = [&](int i) { return GATED ? ld<f32x4>(cgt + CG_WS + 4 * (16 * i + 4 * g)) : (f32x4){1.f, 1.f, 1.f, 1.f}; };
+  auto bet4 = [&](int i) { return ld<f32x4>(sb + LY::O_BETA + 4 * (16 * i + 4 * g)); };
+
   // ---- direct loads
   const char *gk = static_cast<const char *>(p.k);
   const char *gq = static_cast<const char *>(p.q);
   const char *gv = static_cast<const char *>(p.v);
   const char *gdo = static_cast<const char *>(p.dO);
   const size_t rowoff = (row0 * H + h);
-  auto kq_off = [&](int i, int &row) {  // K / Q tile, load i of this wave
-    const int pp = 64 * (w + 4 * i) + l;
-    const int r = pp / (DK / 8), u = (pp % (DK / 8)) ^ swz_s<DK>(r);
-    row = r;
-    return (uint32_t)r * (uint32_t)(H * RB) + 16u * u;
-  };
-  auto issue_kq = [&]() {
+  const size_t sbase_g = ((size_t)cg * H + h) * (size_t)DV;  // row of S / dS for d_v column 0
+  auto issue_kq = [&]() {  // every wave
 #pragma unroll
     for (int i = 0; i < LY::DMA_KQ; ++i) {
-      int r;
-      const uint32_t off = kq_off(i, r);
-      const uint32_t dst = sb + 1024 * (w + 4 * i);
+      const int u = 512 * i + 64 * w + l;
+      const int r = u / (DK / 8), pos = (u % (DK / 8)) ^ swz_s<DK>(r);
+      const uint32_t dst = sb + 16 * (512 * i + 64 * w);
       if (r < L) {
-        dma16(gk + rowoff * RB + off, dst + LY::O_K);
-        dma16(gq + rowoff * RB + off, dst + LY::O_Q);
+        dma16(gk + (rowoff + (size_t)r * H) * RB + 16 * pos, dst + LY::O_K);
+        dma16(gq + (rowoff + (size_t)r * H) * RB + 16 * pos, dst + LY::O_Q);
       }
     }
     if (l < L) {
@@ -192,52 +206,67 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
       if (w == 1) dma4(reinterpret_cast<const char *>(p.beta + rowoff) + 4u * l * H, sb + LY::O_XB);
     }
   };
-  const size_t sbase_g = ((size_t)cg * H + h) * (size_t)DV;  // row of S / dS for d_v column 0
-  auto issue_tile = [&](int j, int buf) {
-    const uint32_t tb = sb + LY::O_T + buf * LY::TB;
-    const int dv0 = 64 * j;
+  // row waves' per-lane byte offsets of the tile loads (base + offset form)
+  const int rw = w - 4;
+  uint32_t vo_v, vo_d, vo_s[LY::DMA_S];
+  {
+    const int u = 64 * rw + l, r = u >> 2, pos = u & 3;  // V, dO: 64 rows x 64 bytes
+    vo_v = (uint32_t)r * (uint32_t)(H * DV * 2) + 16u * (pos ^ swz_v32(r));
+    vo_d = (uint32_t)r * (uint32_t)(H * DV * 2) + 16u * (pos ^ swz_d32(r));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // V and dO: 64 rows x 128 bytes
-      const int pp = 64 * (w + 4 * i) + l;
-      const int r = pp / 8, pos = pp % 8;
-      if (r < L) {
-        dma16(gv + ((rowoff + (size_t)r * H) * DV + dv0) * 2 + 16 * (pos ^ swz_v(r)), tb + LY::T_V + 1024 * (w + 4 * i));
-        dma16(gdo + ((rowoff + (size_t)r * H) * DV + dv0) * 2 + 16 * (pos ^ swz_d(r)), tb + LY::T_DO + 1024 * (w + 4 * i));
-      }
+    for (int i = 0; i < LY::DMA_S; ++i) {  // S, dS: 32 rows x RB bytes
+      const int us = 256 * i + 64 * rw + l;
+      const int rs = us / (DK / 8), ps = (us % (DK / 8)) ^ swz_s<DK>(rs);
+      vo_s[i] = (uint32_t)(rs * RB + 16 * ps);
+    }
+  }
+  const bool vrow = (64 * rw + l) / 4 < L;
+  auto issue_tile = [&](int j) {  // row waves: 64 lanes x DMA_T units of 16 bytes each
+    const uint32_t tb = tbuf(j);
+    const int dv0 = TC * j;
+    if (vrow) {
+      dma16s(gv + (rowoff * DV + dv0) * 2, vo_v, tb + LY::T_V + 16 * (64 * rw));
+      dma16s(gdo + (rowoff * DV + dv0) * 2, vo_d, tb + LY::T_DO + 16 * (64 * rw));
     }
     const char *s0 = reinterpret_cast<const char *>(p.states + (sbase_g + dv0) * DK);
     const char *d0 = reinterpret_cast<const char *>(p.dstates + (sbase_g + dv0) * DK);
 #pragma unroll
-    for (int i = 0; i < LY::DMA_S; ++i) {  // S and dS: 64 rows x RB bytes
-      const int pp = 64 * (w + 4 * i) + l;
-      const int r = pp / (DK / 8), u = (pp % (DK / 8)) ^ swz_s<DK>(r);
-      dma16(s0 + r * RB + 16 * u, tb + LY::T_S + 1024 * (w + 4 * i));
-      dma16(d0 + r * RB + 16 * u, tb + LY::T_DS + 1024 * (w + 4 * i));
+    for (int i = 0; i < LY::DMA_S; ++i) {
+      dma16s(s0, vo_s[i], tb + LY::T_S + 16 * (256 * i + 64 * rw));
+      dma16s(d0, vo_s[i], tb + LY::T_DS + 16 * (256 * i + 64 * rw));
     }
   };
-  // rows past the end of the chunk are zero
-  if (L < CH) {
-    for (int i = L * RB / 16 + threadIdx.x; i < LY::KQ / 16; i += NTHR) {
+
+  // ---- prologue: rows past the end of the chunk are zero
+  if (!full) {
+    for (int i = L * RB / 16 + threadIdx.x; i < LY::KQ / 16; i += BW_THREADS) {
       st<f32x4>(sb + LY::O_K + 16 * i, zero4());
       st<f32x4>(sb + LY::O_Q + 16 * i, zero4());
     }
-    for (int buf = 0; buf < 2; ++buf)
-      for (int i = L * 128 / 16 + threadIdx.x; i < 8192 / 16; i += NTHR) {
+    for (int buf = 0; buf < LY::NBUF; ++buf)
+      for (int i = L * 64 / 16 + threadIdx.x; i < 4096 / 16; i += BW_THREADS) {
         st<f32x4>(sb + LY::O_T + buf * LY::TB + LY::T_V + 16 * i, zero4());
         st<f32x4>(sb + LY::O_T + buf * LY::TB + LY::T_DO + 16 * i, zero4());
       }
   }
   // P^T above the diagonal stays zero
-  for (int i = threadIdx.x; i < RS::P_BYTES / 16; i += NTHR) st<f32x4>(sb + LY::O_RES + RS::O_P + 16 * i, zero4());
+  for (int i = threadIdx.x; i < RS::P_BYTES / 16; i += BW_THREADS) st<f32x4>(ob + RS::O_P + 16 * i, zero4());
   issue_kq();
-  issue_tile(0, 0);
-  wait_vm<0>();
-  if (ntiles > 1) issue_tile(1, 1);
+  if (w >= 4) {
+    issue_tile(0);
+    if (ntiles > 1) {
+      issue_tile(1);
+      if (full) wait_vm<LY::DMA_T>(); else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+  } else {
+    wait_vm<0>();
+  }
   __syncthreads();
 
-  // ---- prep of the chunk (M, P^T, R_ii, gates), one role per wave
-  const uint32_t ob = sb + LY::O_RES;
-  {
+  // ---- prep of the chunk (M, P^T, R_ii, gates) by waves 0..3
+  if (w < 4) {
     if (w == 1) st<float>(sb + LY::O_BETA + 4 * l, l < L ? ld<float>(sb + LY::O_XB + 4 * l) : 0.f);
     float dummy = 1.f;
     const BwdKsw<DK> ksw{lb_frag};
@@ -250,302 +279,364 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chunk_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // gate values of this lane's rows (column phase: rows 16i + 4g + e)
-  const uint32_t cgt = ob + RS::O_CG;
-  auto gam4 = [&](int i) { return GATED ? ld<f32x4>(cgt + CG_GS + 4 * (16 * i + 4 * g)) : (f32x4){1.f, 1.f, 1.f, 1.f}; };
-  auto w4 = [&](int i) { return GATED ? ld<f32x4>(cgt + CG_WS + 4 * (16 * i + 4 * g)) : (f32x4){1.f, 1.f, 1.f, 1.f}; };
-  auto bet4 = [&](int i) { return ld<f32x4>(sb + LY::O_BETA + 4 * (16 * i + 4 * g)); };
+  const uint32_t red = sb + LY::O_RED, fin = sb + LY::O_FIN, dkx = sb + LY::O_DKX;
 
-  // K fragments (rows 16t + n) stay in registers for every tile
-  bf16x8 kf[4][KB];
+  if (w < 4) {
+    // =========================== column waves ===========================
+    const int cs = w >> 1;  // column set: tile columns 16cs .. 16cs + 15
+    bf16x8 kf[4][KB];       // K fragments, rows 16t + n
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kf[t][kb] = ld<bf16x8>(sb + LY::O_K + (lb_frag ^ (64 * kb)) + 16 * t * RB);
+      for (int t = 0; t < 4; ++t) kf[t][kb] = ld<bf16x8>(sb + LY::O_K + (lb_frag ^ (64 * kb)) + 16 * t * RB);
+    const uint32_t sfrag = (16 * cs) * RB;  // S / dS rows of the column set
 
-  // accumulators over d_v (wave w: token rows 16w .. 16w + 15)
-  f32x4 dP[4], dAc[4], dq1[MT], dk1[MT], dk2[MT];
+    if ((w & 1) == 0) {
+      // ------------------------------ F ------------------------------
+      bf16x4 mb[6], tt[4];  // -M_im (A operand, i > m) and T_ii = R_ii (transposed reads)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) dP[t] = dAc[t] = zero4();
+      for (int k = 0; k < 6; ++k) mb[k] = ld<bf16x4>(ob + RS::O_M + 512 * k + lb_m);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) dq1[mt] = dk1[mt] = dk2[mt] = zero4();
-  f32x4 xy[4];  // rowsum(X * Y) partials: rows 16i + 4g + e of this lane's columns
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xy[i] = zero4();
-  float hdh = 0.f;  // <dh, h> partial
-
-  const uint32_t xv = sb + LY::O_X, xy_ = sb + LY::O_X + 8192;  // V'^T, Y^T
-  for (int j = 0; j < ntiles; ++j) {
-    const uint32_t tb = sb + LY::O_T + (j & 1) * LY::TB;
-    if (j > 0) {
-      if (L == CH && j + 1 < ntiles) wait_vm<2 * LY::DMA_S + 4 + 16>(); else wait_vm<0>();
-      __syncthreads();  // tile j loaded by every wave
-    }
-    // ---- column phase: columns 16w + n of the tile
-    {
-      bf16x8 hb[KB], dhb[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint32_t a = (lb_frag ^ (64 * kb)) + 16 * w * RB;
-        hb[kb] = ld<bf16x8>(tb + LY::T_S + a);
-        dhb[kb] = ld<bf16x8>(tb + LY::T_DS + a);
-        hdh = dot8(hb[kb], dhb[kb], hdh);
+      for (int i = 0; i < 4; ++i) tt[i] = ld_tr(ob + RS::O_TT + 512 * i + lb_btr);
+      uint32_t lb_vtr;  // V transposed reads: rows 16t + 4g + e, columns 16cs + 4q
+      {
+        const int r = 4 * g + e4;
+        lb_vtr = r * 64 + 16 * ((2 * cs + (q4 >> 1)) ^ swz_v32(r)) + 8 * (q4 & 1);
       }
-      f32x4 x[4], dvp[4];
+      f32x4 xp[4], xy[4];  // X of the previous tile; rowsum(X * Y) partials (rows 16i + 4g + e)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 yk = zero4(), yd = zero4();
+      for (int i = 0; i < 4; ++i) xp[i] = xy[i] = zero4();
+      for (int s = 0; s <= ntiles; ++s) {
+        if (s > 0) {  // rowsum(X * Y) of tile s - 1 (Y^T handed over by the B wave)
+          const uint32_t yb = xbuf(s - 1) + 4096 + 16 * cs * 128;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          yk = mma32(yk, kf[t][kb], hb[kb]);
-          yd = mma32(yd, kf[t][kb], dhb[kb]);
+          for (int i = 0; i < 4; ++i) {
+            const bf16x4 yv = ld<bf16x4>(yb + (lb_xw ^ (32 * i)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xy[i][e] += xp[i][e] * bf2f(yv[e]);
+          }
         }
-        const bf16x4 vr = ld_tr(tb + LY::T_V + 16 * t * 128 + lb_vtr);
-        const f32x4 gm = gam4(t);
+        if (s < ntiles) {
+          const uint32_t tb = tbuf(s);
+          bf16x8 hb[KB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[t][e] = bf2f(vr[e]) - gm[e] * yk[e];
-        dvp[t] = w4(t) * yd;
+          for (int kb = 0; kb < KB; ++kb) hb[kb] = ld<bf16x8>(tb + LY::T_S + sfrag + (lb_frag ^ (64 * kb)));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            f32x4 yk = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) yk = mma32(yk, kf[t][kb], hb[kb]);
+            const bf16x4 vr = ld_tr(tb + LY::T_V + 1024 * t + lb_vtr);
+            const f32x4 gm = gam4(t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xp[t][e] = bf2f(vr[e]) - gm[e] * yk[e];
+          }
+          // V'_i = R_ii diag(beta_i) (X_i - sum_{m<i} M_im V'_m)
+          bf16x4 vb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 acc = xp[i];
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc = mma16(acc, mb[m_block(i, m)], vb[m]);
+            acc = acc * bet4(i);
+            vb[i] = cvt4(mma16(zero4(), tt[i], cvt4(acc)));
+          }
+          const uint32_t xv = xbuf(s) + 16 * cs * 128;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st<bf16x4>(xv + (lb_xw ^ (32 * i)), vb[i]);
+        }
+        mfma_settle();
+        __syncthreads();
       }
-      // dV' += P^T dO (token blocks kb >= t / 2)
-      bf16x8 dob[2];
+      // rowsum(X * Y) of this wave's columns
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        dob[kb] = cat(ld_tr(tb + LY::T_DO + 32 * kb * 128 + lb_dtr[0]), ld_tr(tb + LY::T_DO + 32 * kb * 128 + lb_dtr[1]));
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int kb = t >> 1; kb < 2; ++kb) dvp[t] = mma32(dvp[t], ld<bf16x8>(ob + RS::O_P + pt_frag(t, kb, l)), dob[kb]);
-      // V'_i = R_ii diag(beta_i) (X_i - sum_{m<i} M_im V'_m)
-      bf16x4 vb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 acc = x[i];
-#pragma unroll
-        for (int m = 0; m < i; ++m) acc = mma16(acc, ld<bf16x4>(ob + RS::O_M + 512 * m_block(i, m) + lb_m), vb[m]);
-        acc = acc * bet4(i);
-        vb[i] = cvt4(mma16(zero4(), ld_tr(ob + RS::O_TT + 512 * i + lb_btr), cvt4(acc)));
-      }
-      // Y_i = R_ii^T (dV'_i - sum_{m>i} M_mi^T dX_m), dX = diag(beta) Y
-      f32x4 y[4];
-      bf16x4 dxb[4];
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        f32x4 acc = dvp[i];
-#pragma unroll
-        for (int m = i + 1; m < 4; ++m) acc = mma16(acc, ld_tr(ob + RS::O_M + 512 * m_block(m, i) + lb_btr), dxb[m]);
-        y[i] = mma16(zero4(), ld<bf16x4>(ob + RS::O_TT + 512 * i + lb_m), cvt4(acc));
-        const f32x4 dx = y[i] * bet4(i);
-        dxb[i] = cvt4(dx);
-        xy[i] = xy[i] + x[i] * y[i];
-        // dv
-        const int col = 64 * j + 16 * w + n;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * i + 4 * g + e;
-          if (r < L) p.dv[((row0 + r) * H + h) * (size_t)DV + col] = dx[e];
+          const float sm = sum16(xy[i][e]);
+          if (n == 0) st<float>(red + 1024 + 256 * cs + 4 * (16 * i + 4 * g + e), sm);
         }
-      }
-      // hand V'^T and Y^T to the row phase
+    } else {
+      // ------------------------------ B ------------------------------
+      bf16x8 ptf[6];        // P^T fragments (t, kb >= t / 2): (0,0) (0,1) (1,0) (1,1) (2,1) (3,1)
+      bf16x4 mtb[6], rt[4];  // -M_mi^T (transposed reads) and R_ii^T
+      ptf[0] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 0, l));
+      ptf[1] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 1, l));
+      ptf[2] = ld<bf16x8>(ob + RS::O_P + pt_frag(1, 0, l));
+      ptf[3] = ld<bf16x8>(ob + RS::O_P + pt_frag(1, 1, l));
+      ptf[4] = ld<bf16x8>(ob + RS::O_P + pt_frag(2, 1, l));
+      ptf[5] = ld<bf16x8>(ob + RS::O_P + pt_frag(3, 1, l));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st<bf16x4>(xv + 16 * w * 128 + (lb_xw ^ (32 * i)), vb[i]);
-        st<bf16x4>(xy_ + 16 * w * 128 + (lb_xw ^ (32 * i)), cvt4(y[i]));
+      for (int k = 0; k < 6; ++k) mtb[k] = ld_tr(ob + RS::O_M + 512 * k + lb_btr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rt[i] = ld<bf16x4>(ob + RS::O_TT + 512 * i + lb_m);
+      uint32_t lb_dtr[2];  // dO transposed reads, rows 8g + 4hh + e (+ 32 kb), columns 16cs + 4q
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = 8 * g + 4 * hh + e4;
+        lb_dtr[hh] = r * 64 + 16 * ((2 * cs + (q4 >> 1)) ^ swz_d32(r)) + 8 * (q4 & 1);
+      }
+      for (int s = 0; s <= ntiles; ++s) {
+        if (s < ntiles) {
+          const uint32_t tb = tbuf(s);
+          bf16x8 dhb[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) dhb[kb] = ld<bf16x8>(tb + LY::T_DS + sfrag + (lb_frag ^ (64 * kb)));
+          f32x4 dvp[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            f32x4 yd = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) yd = mma32(yd, kf[t][kb], dhb[kb]);
+            dvp[t] = w4(t) * yd;
+          }
+          // dV' += P^T dO (token blocks kb >= t / 2)
+          bf16x8 dob[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            dob[kb] = cat(ld_tr(tb + LY::T_DO + 2048 * kb + lb_dtr[0]), ld_tr(tb + LY::T_DO + 2048 * kb + lb_dtr[1]));
+          dvp[0] = mma32(mma32(dvp[0], ptf[0], dob[0]), ptf[1], dob[1]);
+          dvp[1] = mma32(mma32(dvp[1], ptf[2], dob[0]), ptf[3], dob[1]);
+          dvp[2] = mma32(dvp[2], ptf[4], dob[1]);
+          dvp[3] = mma32(dvp[3], ptf[5], dob[1]);
+          // Y_i = R_ii^T (dV'_i - sum_{m>i} M_mi^T dX_m), dX = diag(beta) Y
+          f32x4 y[4];
+          bf16x4 dxb[4];
+          float *dvb = p.dv + (row0 * H + h) * (size_t)DV + TC * s;  // wave-uniform
+#pragma unroll
+          for (int i = 3; i >= 0; --i) {
+            f32x4 acc = dvp[i];
+#pragma unroll
+            for (int m = i + 1; m < 4; ++m) acc = mma16(acc, mtb[m_block(m, i)], dxb[m]);
+            y[i] = mma16(zero4(), rt[i], cvt4(acc));
+            const f32x4 dx = y[i] * bet4(i);
+            dxb[i] = cvt4(dx);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * i + 4 * g + e;
+              if (r < L) dvb[(uint32_t)(r * H * DV + 16 * cs + n)] = dx[e];
+            }
+          }
+          const uint32_t yb = xbuf(s) + 4096 + 16 * cs * 128;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st<bf16x4>(yb + (lb_xw ^ (32 * i)), cvt4(y[i]));
+        }
+        mfma_settle();
+        __syncthreads();
       }
     }
-    __syncthreads();  // V'^T, Y^T complete
-    // ---- row phase: token rows 16w + n
+    __syncthreads();  // dPG^T, F^T and the reductions are complete
+
+    // dk (column part) of token rows 16w + 4g + e: dPG^T Q + F^T K
     {
-      bf16x8 dof[2], yf[2], vf[2];
+      bf16x8 pgt[2], ft[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        dof[kb] = ld<bf16x8>(tb + LY::T_DO + (lb_dfrag ^ (64 * kb)));
-        const uint32_t a0 = 32 * kb * 128 + (lb_xtr[0] ^ (32 * w)), a1 = 32 * kb * 128 + (lb_xtr[1] ^ (32 * w));
-        yf[kb] = cat(ld_tr(xy_ + a0), ld_tr(xy_ + a1));
-        vf[kb] = cat(ld_tr(xv + a0), ld_tr(xv + a1));
+        pgt[kb] = ld<bf16x8>(fin + pt_frag(w, kb, l));
+        ft[kb] = ld<bf16x8>(fin + 8192 + pt_frag(w, kb, l));
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (jt > w) break;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint32_t a0 = 32 * kb * 128 + (lb_xtr[0] ^ (32 * jt)), a1 = 32 * kb * 128 + (lb_xtr[1] ^ (32 * jt));
-          const bf16x8 vt = cat(ld_tr(xv + a0), ld_tr(xv + a1));
-          dP[jt] = mma32(dP[jt], dof[kb], vt);
-          dAc[jt] = mma32(dAc[jt], yf[kb], vt);
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 dk = zero4();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
-          const bf16x8 sf = cat(ld_tr(tb + LY::T_S + a0), ld_tr(tb + LY::T_S + a1));
-          const bf16x8 dsf = cat(ld_tr(tb + LY::T_DS + a0), ld_tr(tb + LY::T_DS + a1));
-          dq1[mt] = mma32(dq1[mt], dof[kb], sf);
-          dk1[mt] = mma32(dk1[mt], yf[kb], sf);
-          dk2[mt] = mma32(dk2[mt], vf[kb], dsf);
+          const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
+          const bf16x8 qt = cat(ld_tr(sb + LY::O_Q + a0), ld_tr(sb + LY::O_Q + a1));
+          dk = mma32(dk, pgt[kb], qt);
+          dk = mma32(dk, ft[kb], kt);
         }
+        st<f32x4>(dkx + 16 * ((w * MT + mt) * 64 + l), dk);
+      }
+    }
+    // dbeta, db -> dg (reverse cumulative sum inside the chunk)
+    if (w == 0) {
+      const int r = l;
+      float ce = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) ce += ld<float>(red + 256 * ww + 4 * r);
+      const float xyr = ld<float>(red + 1024 + 4 * r) + ld<float>(red + 1280 + 4 * r);
+      float db = ld<float>(red + 2048 + 4 * r) - ce;
+      if (r == CH - 1) {
+        float s3t = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) s3t += ld<float>(red + 2560 + 4 * ww);
+        const float g63 = GATED ? ld<float>(cgt + CG_GS + 4 * (CH - 1)) : 1.f;
+        db += s3t + g63 * ld<float>(red + 2576);
+      }
+      const float incl = wave_incl_scan(db);
+      const float total = __shfl(incl, 63, 64);
+      if (r < L) {
+        const size_t idx = (row0 + r) * H + h;
+        p.dbeta[idx] = xyr + ld<float>(red + 2304 + 4 * r);
+        if (GATED) p.dg[idx] = total - incl + db;  // sum_{r' >= r} db_r'
+      }
     }
     mfma_settle();
-    __syncthreads();  // tile j and the hand-over buffers are free again
-    if (j + 2 < ntiles) issue_tile(j + 2, j & 1);
-  }
+    __syncthreads();  // the column part of dk is in LDS
+  } else {
+    // ============================= row waves =============================
+    const int rho = w == 4 ? 3 : w == 5 ? 0 : w == 6 ? 2 : 1;  // token rows 16rho .. 16rho + 15
+    const bool hdh_wave = rho == 0;
+    const uint32_t lb_dfrag = (16 * rho + n) * 64 + 16 * (g ^ swz_d32(n));  // dO frag, row 16rho + n
+    f32x4 dP[4], dAc[4], dq1[MT], dk1[MT], dk2[MT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dP[t] = dAc[t] = zero4();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) dq1[mt] = dk1[mt] = dk2[mt] = zero4();
+    float hdh = 0.f;  // <dh, h> partial (one wave)
+    for (int s = 0; s <= ntiles; ++s) {
+      if (s + 2 < ntiles) issue_tile(s + 2);
+      if (s > 0) {
+        const int j = s - 1;
+        const uint32_t tb = tbuf(j), xv = xbuf(j), xyb = xbuf(j) + 4096;
+        const bf16x8 dof = ld<bf16x8>(tb + LY::T_DO + lb_dfrag);
+        const bf16x8 yf = cat(ld_tr(xyb + (lb_xtr[0] ^ (32 * rho))), ld_tr(xyb + (lb_xtr[1] ^ (32 * rho))));
+        const bf16x8 vf = cat(ld_tr(xv + (lb_xtr[0] ^ (32 * rho))), ld_tr(xv + (lb_xtr[1] ^ (32 * rho))));
+        // every token block: the blocks above the diagonal (jt > rho) are masked in the final phase
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const bf16x8 vt = cat(ld_tr(xv + (lb_xtr[0] ^ (32 * jt))), ld_tr(xv + (lb_xtr[1] ^ (32 * jt))));
+          dP[jt] = mma32(dP[jt], dof, vt);
+          dAc[jt] = mma32(dAc[jt], yf, vt);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint32_t a0 = lb_str[0] ^ (32 * mt), a1 = lb_str[1] ^ (32 * mt);
+          const bf16x8 sf = cat(ld_tr(tb + LY::T_S + a0), ld_tr(tb + LY::T_S + a1));
+          const bf16x8 dsf = cat(ld_tr(tb + LY::T_DS + a0), ld_tr(tb + LY::T_DS + a1));
+          dq1[mt] = mma32(dq1[mt], dof, sf);
+          dk1[mt] = mma32(dk1[mt], yf, sf);
+          dk2[mt] = mma32(dk2[mt], vf, dsf);
+          if (hdh_wave) hdh = dot8(sf, dsf, hdh);
+        }
+      }
+      // tile s + 1 (and everything older) lands before the barrier; tile s + 2 may stay in flight
+      if (s + 2 < ntiles && full) wait_vm<LY::DMA_T>();
+      else wait_vm<0>();
+      mfma_settle();
+      __syncthreads();
+    }
 
-  // ---- final phase (wave w: rows r = 16w + 4g + e)
-  const uint32_t fin = sb + LY::O_T;              // dPG^T and F^T, P^T layout
-  const uint32_t red = sb + LY::O_T + LY::TB;     // reductions
-  const f32x4 gam_r = gam4(w), w_r = w4(w), bet_r = bet4(w);
-  const f32x4 bl_r = GATED ? ld<f32x4>(cgt + CG_BL + 4 * (16 * w + 4 * g)) : zero4();
-  f32x4 erow = zero4(), dbr = zero4();
+    // ---- final phase (row wave rho: rows r = 16rho + 4g + e)
+    const f32x4 gam_r = gam4(rho), w_r = w4(rho), bet_r = bet4(rho);
+    const f32x4 bl_r = GATED ? ld<f32x4>(cgt + CG_BL + 4 * (16 * rho + 4 * g)) : zero4();
+    f32x4 erow = zero4(), dbr = zero4();
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    f32x4 dpg = zero4(), f = zero4();
-    float ce = 0.f;
-    if (jt <= w) {
-      const int jj = 16 * jt + n;
-      const float blj = GATED ? ld<float>(cgt + CG_BL + 4 * jj) : 0.f;
-      const bf16x4 pv = ld<bf16x4>(ob + RS::O_P + pt_quad(jt, w, l));  // P[r][j]
-      f32x4 mv;                                                        // M[r][j]
-      if (jt < w) {
-        const bf16x4 mm = ld_tr(ob + RS::O_M + 512 * m_block(w, jt) + lb_btr);
+    for (int jt = 0; jt < 4; ++jt) {
+      f32x4 dpg = zero4(), f = zero4();
+      float ce = 0.f;
+      if (jt <= rho) {
+        const int jj = 16 * jt + n;
+        const float blj = GATED ? ld<float>(cgt + CG_BL + 4 * jj) : 0.f;
+        const bf16x4 pv = ld<bf16x4>(ob + RS::O_P + pt_quad(jt, rho, l));  // P[r][j]
+        f32x4 mv;                                                          // M[r][j]
+        if (jt < rho) {
+          const bf16x4 mm = ld_tr(ob + RS::O_M + 512 * m_block(rho, jt) + lb_btr);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mv[e] = -bf2f(mm[e]);
-      } else {
-        const bf16x4 mm = ld<bf16x4>(ob + RS::O_M + 512 * (6 + w) + lb_m);
+          for (int e = 0; e < 4; ++e) mv[e] = -bf2f(mm[e]);
+        } else {
+          const bf16x4 mm = ld<bf16x4>(ob + RS::O_M + 512 * (6 + rho) + lb_m);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mv[e] = bf2f(mm[e]);
+          for (int e = 0; e < 4; ++e) mv[e] = bf2f(mm[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rho + 4 * g + e;
+          const float gm = GATED ? fexp2(jj <= r ? bl_r[e] - blj : 0.f) : 1.f;
+          dpg[e] = (jj <= r) ? dP[jt][e] * gm : 0.f;
+          const float da = (jj < r) ? -dAc[jt][e] : 0.f;
+          f[e] = da * gm * bet_r[e];
+          dbr[e] += da * mv[e];
+          const float ev = dP[jt][e] * bf2f(pv[e]) + da * bet_r[e] * mv[e];
+          erow[e] += ev;
+          ce += ev;
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * g + e;
-        const float gm = GATED ? fexp2(jj <= r ? bl_r[e] - blj : 0.f) : 1.f;
-        dpg[e] = (jj <= r) ? dP[jt][e] * gm : 0.f;
-        const float da = (jj < r) ? -dAc[jt][e] : 0.f;
-        f[e] = da * gm * bet_r[e];
-        dbr[e] += da * mv[e];
-        const float ev = dP[jt][e] * bf2f(pv[e]) + da * bet_r[e] * mv[e];
-        erow[e] += ev;
-        ce += ev;
-      }
+      st<bf16x4>(fin + pt_quad(jt, rho, l), cvt4(dpg));
+      st<bf16x4>(fin + 8192 + pt_quad(jt, rho, l), cvt4(f));
+      ce = sum4g(ce);
+      if (g == 0) st<float>(red + 256 * rho + 4 * (16 * jt + n), ce);  // colsum(E) of these rows
     }
-    st<bf16x4>(fin + pt_quad(jt, w, l), cvt4(dpg));
-    st<bf16x4>(fin + 8192 + pt_quad(jt, w, l), cvt4(f));
-    ce = sum4g(ce);
-    if (g == 0) st<float>(red + 256 * w + 4 * (16 * jt + n), ce);  // colsum(E) of wave w
-  }
-  // rowsum(X * Y) of this wave's columns, and the scalars
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float s = sum16(xy[i][e]);
-      if (n == 0) st<float>(red + 1024 + 256 * w + 4 * (16 * i + 4 * g + e), s);
+    // row terms: gamma_r q_r . DQ_r - gamma_r beta_r k_r . DY_r - w_r k_r . DH_r
+    uint32_t lb_rtr;  // K, Q transposed reads: rows 16rho + 4g + e, columns 16mt + 4q
+    {
+      const int r = 4 * g + e4, s = swz_s<DK>(r);
+      lb_rtr = (16 * rho + r) * RB + 8 * q4 + 32 * (s >> 1);
     }
-  hdh = wave_sum(hdh);
-  // row terms: gamma_r q_r . DQ_r - gamma_r beta_r k_r . DY_r - w_r k_r . DH_r
-  f32x4 rowt = zero4();
-  float s3 = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const bf16x4 qv = ld_tr(sb + LY::O_Q + (lb_rtr ^ (32 * mt)));
-    const bf16x4 kv = ld_tr(sb + LY::O_K + (lb_rtr ^ (32 * mt)));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float kdh = bf2f(kv[e]) * dk2[mt][e];
-      rowt[e] += gam_r[e] * (bf2f(qv[e]) * dq1[mt][e] - bet_r[e] * bf2f(kv[e]) * dk1[mt][e]) - w_r[e] * kdh;
-      s3 += w_r[e] * kdh;
-    }
-  }
-  s3 = wave_sum(s3);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float rt = sum16(rowt[e] + erow[e]);
-    const float db = sum16(dbr[e]);
-    if (n == 0) {
-      st<float>(red + 2048 + 4 * (16 * w + 4 * g + e), rt);
-      st<float>(red + 2304 + 4 * (16 * w + 4 * g + e), db);
-    }
-  }
-  if (l == 0) {
-    st<float>(red + 2560 + 4 * w, s3);
-    st<float>(red + 2576 + 4 * w, hdh);
-  }
-  __syncthreads();
-
-  // dq = diag(gamma) dO h^T + dPG K ;
-  // dk = dPG^T Q - diag(gamma beta) Y h^T + diag(w) V' dh^T + F K + F^T K
-  {
-    bf16x8 pgr[2], pgt[2], fr[2], ft[2];  // A operands: rows r (dPG, F), rows j (dPG^T, F^T)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // rows 16w + n of dPG: columns j = slots of kb, read transposed from dPG^T
-      bf16x4 t0, t1, u0, u1;
-      {
-        const int r0 = 32 * kb + 8 * g + e4, r1 = r0 + 4;  // dPG^T rows j
-        const int c = 16 * w + 4 * q4;                       // columns r
-        const uint32_t a0 = 128 * r0 + 16 * ((c / 8) ^ swz_p128(r0 & 15)) + 8 * ((c % 8) / 4);
-        const uint32_t a1 = 128 * r1 + 16 * ((c / 8) ^ swz_p128(r1 & 15)) + 8 * ((c % 8) / 4);
-        t0 = ld_tr(fin + a0);
-        t1 = ld_tr(fin + a1);
-        u0 = ld_tr(fin + 8192 + a0);
-        u1 = ld_tr(fin + 8192 + a1);
-      }
-      pgr[kb] = cat(t0, t1);
-      fr[kb] = cat(u0, u1);
-      pgt[kb] = ld<bf16x8>(fin + pt_frag(w, kb, l));
-      ft[kb] = ld<bf16x8>(fin + 8192 + pt_frag(w, kb, l));
-    }
+    f32x4 rowt = zero4();
+    float s3 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      f32x4 dq = gam_r * dq1[mt];
-      f32x4 dk = w_r * dk2[mt] - gam_r * bet_r * dk1[mt];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
-        const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
-        const bf16x8 qt = cat(ld_tr(sb + LY::O_Q + a0), ld_tr(sb + LY::O_Q + a1));
-        dq = mma32(dq, pgr[kb], kt);
-        dk = mma32(dk, pgt[kb], qt);
-        dk = mma32(dk, fr[kb], kt);
-        dk = mma32(dk, ft[kb], kt);
-      }
+      const bf16x4 qv = ld_tr(sb + LY::O_Q + (lb_rtr ^ (32 * mt)));
+      const bf16x4 kv = ld_tr(sb + LY::O_K + (lb_rtr ^ (32 * mt)));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * g + e;
-        if (r < L) {
-          const size_t o = ((row0 + r) * H + h) * (size_t)DK + 16 * mt + n;
-          p.dq[o] = dq[e];
-          p.dk[o] = dk[e];
+        const float kdh = bf2f(kv[e]) * dk2[mt][e];
+        rowt[e] += gam_r[e] * (bf2f(qv[e]) * dq1[mt][e] - bet_r[e] * bf2f(kv[e]) * dk1[mt][e]) - w_r[e] * kdh;
+        s3 += w_r[e] * kdh;
+      }
+    }
+    s3 = wave_sum(s3);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float rt = sum16(rowt[e] + erow[e]);
+      const float db = sum16(dbr[e]);
+      if (n == 0) {
+        st<float>(red + 2048 + 4 * (16 * rho + 4 * g + e), rt);
+        st<float>(red + 2304 + 4 * (16 * rho + 4 * g + e), db);
+      }
+    }
+    if (l == 0) st<float>(red + 2560 + 4 * rho, s3);
+    if (hdh_wave) {
+      hdh = wave_sum(hdh);
+      if (l == 0) st<float>(red + 2576, hdh);
+    }
+    mfma_settle();
+    __syncthreads();  // dPG^T, F^T and the reductions are complete
+
+    // dq = diag(gamma) dO h^T + dPG K ;  dk (row part) = diag(w) V' dh^T - diag(gamma beta) Y h^T + F K
+    f32x4 dkr[MT];
+    {
+      bf16x8 pgr[2], fr[2];  // A operands: rows r of dPG and F, read transposed from dPG^T, F^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r0 = 32 * kb + 8 * g + e4, r1 = r0 + 4;  // dPG^T rows j
+        const int cc = 16 * rho + 4 * q4;                   // columns r
+        const uint32_t a0 = 128 * r0 + 16 * ((cc / 8) ^ swz_p128(r0 & 15)) + 8 * ((cc % 8) / 4);
+        const uint32_t a1 = 128 * r1 + 16 * ((cc / 8) ^ swz_p128(r1 & 15)) + 8 * ((cc % 8) / 4);
+        pgr[kb] = cat(ld_tr(fin + a0), ld_tr(fin + a1));
+        fr[kb] = cat(ld_tr(fin + 8192 + a0), ld_tr(fin + 8192 + a1));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 dq = gam_r * dq1[mt];
+        f32x4 dk = w_r * dk2[mt] - gam_r * bet_r * dk1[mt];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
+          const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
+          dq = mma32(dq, pgr[kb], kt);
+          dk = mma32(dk, fr[kb], kt);
+        }
+        dkr[mt] = dk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rho + 4 * g + e;
+          if (r < L) p.dq[((row0 + r) * H + h) * (size_t)DK + 16 * mt + n] = dq[e];
         }
       }
     }
-  }
-  // dbeta, db -> dg (reverse cumulative sum inside the chunk)
-  if (w == 0) {
-    const int r = l;
-    float ce = 0.f, xyr = 0.f;
+    mfma_settle();
+    __syncthreads();  // the column part of dk is in LDS
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      ce += ld<float>(red + 256 * ww + 4 * r);
-      xyr += ld<float>(red + 1024 + 256 * ww + 4 * r);
-    }
-    float db = ld<float>(red + 2048 + 4 * r) - ce;
-    if (r == CH - 1) {
-      float s3t = 0.f, hdt = 0.f;
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 dk = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        s3t += ld<float>(red + 2560 + 4 * ww);
-        hdt += ld<float>(red + 2576 + 4 * ww);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rho + 4 * g + e;
+        if (r < L) p.dk[((row0 + r) * H + h) * (size_t)DK + 16 * mt + n] = dk[e];
       }
-      const float g63 = GATED ? ld<float>(cgt + CG_GS + 4 * (CH - 1)) : 1.f;
-      db += s3t + g63 * hdt;
-    }
-    const float incl = wave_incl_scan(db);
-    const float total = __shfl(incl, 63, 64);
-    if (r < L) {
-      const size_t idx = (row0 + r) * H + h;
-      p.dbeta[idx] = xyr + ld<float>(red + 2304 + 4 * r);
-      if (GATED) p.dg[idx] = total - incl + db;  // sum_{r' >= r} db_r'
     }
   }
 }
@@ -559,7 +650,8 @@ hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const int grid = p.total_chunks * p.H;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHR), smem, stream, p);
+  if (p.DV % TC != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BW_THREADS), smem, stream, p);
   return hipGetLastError();
 }
 

@@ -34,18 +34,21 @@
 // Organisation.  d_v is walked in 32-column tiles through a two-stage
 // pipeline; in step s
 //   column waves 0..3  take tile s.  Wave 2c ("F") owns tile columns
-//                      16c .. 16c + 15 for X = V - gamma K h and the forward
-//                      substitution (V'); wave 2c + 1 ("B") the same columns
-//                      for dV' = w K dh + P^T dO, the backward substitution
-//                      (Y), dX and dv.  They hand V'^T and Y^T to the row
-//                      waves through one of two LDS buffers.
+//                      16c .. 16c + 15 for X = V - gamma K h and
+//                      V' = R diag(beta) X; wave 2c + 1 ("B") the same
+//                      columns for dV' = w K dh + P^T dO, Y = R^T dV', dX and
+//                      dv.  They hand V'^T and Y^T to the row waves through
+//                      one of two LDS buffers.
 //   row waves 4..7     take tile s - 1: each owns 16 token rows of the
 //                      products contracting over the tile's columns (dP, dA,
 //                      dO h^T, Y h^T, V' dh^T), accumulated in registers over
 //                      all tiles, and issues the direct loads of tile s + 2.
-// Wave w and wave w + 4 share a SIMD, so a column wave's dependent chain of
-// small MFMAs and a row wave's stream of independent ones fill each other's
-// stalls.  Each role runs its own loop with one barrier per step; the roles
+// R = (I + A)^-1 is formed once per chunk, in 16 x 16 blocks: the prep
+// inverts the diagonal blocks by substitution, then three row waves compute
+// the blocks below the diagonal (one block column each, by the block
+// recurrence of the inverse of a lower-triangular matrix), so that V' and Y
+// are ten independent block products per tile instead of a chain of block
+// substitutions.  Wave w and wave w + 4 share a SIMD.  Each role runs its own loop with one barrier per step; the roles
 // keep their own registers (a wave's state never holds another role's).
 // Tiles arrive two steps ahead in a ring of four LDS buffers.  After the last
 // step the row waves form dPG = dP * Gamma and F and write them transposed;
@@ -108,18 +111,6 @@ struct BwdKsw {
   __device__ __forceinline__ uint32_t frag(int t, int kb) const { return (frag_base ^ (64 * kb)) + 16 * t * 2 * DK; }
 };
 
-// sum over the 16 lanes of a row of 16 (same lane group)
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-// sum over the 4 lane groups (same column n)
-__device__ __forceinline__ float sum4g(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
 
 template <int DK, bool GATED>
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
@@ -279,6 +270,35 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   }
   __syncthreads();
 
+  // ---- the blocks of R = (I + A)^-1 below the diagonal, one block column per
+  // wave (waves 4..6), from R_ii and -M (the prep's results):
+  //   R_ij = R_ii diag(beta_i) sum_{m=j}^{i-1} (-M_im) R_mj,   i > j,
+  // stored transposed (like R_ii^T) in the S part of the fourth tile buffer,
+  // which the ring does not load before step 1 and then overwrites whole
+  // (unlike its V and dO parts, whose rows past a partial chunk stay zero);
+  // the column waves keep them in registers.
+  const uint32_t rbuf = tbuf(3) + LY::T_S;
+  static_assert(6 * 512 <= LY::ST, "R blocks fit in a state tile");
+  auto rcol = [&](auto j_c) {  // straight-line per block column (MFMA results read without branches)
+    constexpr int J = decltype(j_c)::value;
+    bf16x4 rc[4];  // R_mJ as B operands (lane (n, g): rows 4g .. 4g + 3 of column n)
+    rc[J] = ld<bf16x4>(ob + RS::O_TT + 512 * J + lb_m);
+#pragma unroll
+    for (int i = J + 1; i < 4; ++i) {
+      f32x4 z = zero4();
+#pragma unroll
+      for (int m = J; m < i; ++m) z = mma16(z, ld<bf16x4>(ob + RS::O_M + 512 * m_block(i, m) + lb_m), rc[m]);
+      z = z * bet4(i);
+      rc[i] = cvt4(mma16(zero4(), ld_tr(ob + RS::O_TT + 512 * i + lb_btr), cvt4(z)));
+      st<bf16x4>(rbuf + 512 * m_block(i, J) + lb_m, rc[i]);
+    }
+    mfma_settle();
+  };
+  if (w == 4) rcol(I0{});
+  else if (w == 5) rcol(I1{});
+  else if (w == 6) rcol(I2{});
+  __syncthreads();
+
   const uint32_t red = sb + LY::O_RED, fin = sb + LY::O_FIN, dkx = sb + LY::O_DKX;
 
   if (w < 4) {
@@ -293,11 +313,12 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 
     if ((w & 1) == 0) {
       // ------------------------------ F ------------------------------
-      bf16x4 mb[6], tt[4];  // -M_im (A operand, i > m) and T_ii = R_ii (transposed reads)
+      bf16x4 ra[10];  // R_im, m <= i, as A operands (transposed reads of the stored R^T blocks)
 #pragma unroll
-      for (int k = 0; k < 6; ++k) mb[k] = ld<bf16x4>(ob + RS::O_M + 512 * k + lb_m);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tt[i] = ld_tr(ob + RS::O_TT + 512 * i + lb_btr);
+        for (int m = 0; m <= i; ++m)
+          ra[i * (i + 1) / 2 + m] = ld_tr((m == i ? ob + RS::O_TT + 512 * i : rbuf + 512 * m_block(i, m)) + lb_btr);
       uint32_t lb_vtr;  // V transposed reads: rows 16t + 4g + e, columns 16cs + 4q
       {
         const int r = 4 * g + e4;
@@ -331,15 +352,16 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) xp[t][e] = bf2f(vr[e]) - gm[e] * yk[e];
           }
-          // V'_i = R_ii diag(beta_i) (X_i - sum_{m<i} M_im V'_m)
-          bf16x4 vb[4];
+          // V' = R diag(beta) X: V'_i = sum_{m<=i} R_im (beta_m X_m)
+          bf16x4 bx[4], vb[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) bx[m] = cvt4(xp[m] * bet4(m));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            f32x4 acc = xp[i];
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m < i; ++m) acc = mma16(acc, mb[m_block(i, m)], vb[m]);
-            acc = acc * bet4(i);
-            vb[i] = cvt4(mma16(zero4(), tt[i], cvt4(acc)));
+            for (int m = 0; m <= i; ++m) acc = mma16(acc, ra[i * (i + 1) / 2 + m], bx[m]);
+            vb[i] = cvt4(acc);
           }
           const uint32_t xv = xbuf(s) + 16 * cs * 128;
 #pragma unroll
@@ -353,13 +375,13 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float sm = sum16(xy[i][e]);
+          const float sm = row_sum16(xy[i][e]);
           if (n == 0) st<float>(red + 1024 + 256 * cs + 4 * (16 * i + 4 * g + e), sm);
         }
     } else {
       // ------------------------------ B ------------------------------
       bf16x8 ptf[6];        // P^T fragments (t, kb >= t / 2): (0,0) (0,1) (1,0) (1,1) (2,1) (3,1)
-      bf16x4 mtb[6], rt[4];  // -M_mi^T (transposed reads) and R_ii^T
+      bf16x4 rb[10];  // (R_mi)^T, m >= i, as A operands (rows of the stored R^T blocks), index m(m+1)/2 + i
       ptf[0] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 0, l));
       ptf[1] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 1, l));
       ptf[2] = ld<bf16x8>(ob + RS::O_P + pt_frag(1, 0, l));
@@ -367,9 +389,10 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       ptf[4] = ld<bf16x8>(ob + RS::O_P + pt_frag(2, 1, l));
       ptf[5] = ld<bf16x8>(ob + RS::O_P + pt_frag(3, 1, l));
 #pragma unroll
-      for (int k = 0; k < 6; ++k) mtb[k] = ld_tr(ob + RS::O_M + 512 * k + lb_btr);
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rt[i] = ld<bf16x4>(ob + RS::O_TT + 512 * i + lb_m);
+        for (int i = 0; i <= m; ++i)
+          rb[m * (m + 1) / 2 + i] = ld<bf16x4>((m == i ? ob + RS::O_TT + 512 * i : rbuf + 512 * m_block(m, i)) + lb_m);
       uint32_t lb_dtr[2];  // dO transposed reads, rows 8g + 4hh + e (+ 32 kb), columns 16cs + 4q
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -399,18 +422,19 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           dvp[1] = mma32(mma32(dvp[1], ptf[2], dob[0]), ptf[3], dob[1]);
           dvp[2] = mma32(dvp[2], ptf[4], dob[1]);
           dvp[3] = mma32(dvp[3], ptf[5], dob[1]);
-          // Y_i = R_ii^T (dV'_i - sum_{m>i} M_mi^T dX_m), dX = diag(beta) Y
+          // Y = R^T dV': Y_i = sum_{m>=i} (R_mi)^T dV'_m;  dX = diag(beta) Y
+          bf16x4 db16[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) db16[m] = cvt4(dvp[m]);
           f32x4 y[4];
-          bf16x4 dxb[4];
           float *dvb = p.dv + (row0 * H + h) * (size_t)DV + TC * s;  // wave-uniform
 #pragma unroll
           for (int i = 3; i >= 0; --i) {
-            f32x4 acc = dvp[i];
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int m = i + 1; m < 4; ++m) acc = mma16(acc, mtb[m_block(m, i)], dxb[m]);
-            y[i] = mma16(zero4(), rt[i], cvt4(acc));
+            for (int m = 3; m >= i; --m) acc = mma16(acc, rb[m * (m + 1) / 2 + i], db16[m]);
+            y[i] = acc;
             const f32x4 dx = y[i] * bet4(i);
-            dxb[i] = cvt4(dx);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 16 * i + 4 * g + e;
@@ -465,7 +489,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         db += s3t + g63 * ld<float>(red + 2576);
       }
       const float incl = wave_incl_scan(db);
-      const float total = __shfl(incl, 63, 64);
+      const float total = lane_val(incl, 63);
       if (r < L) {
         const size_t idx = (row0 + r) * H + h;
         p.dbeta[idx] = xyr + ld<float>(red + 2304 + 4 * r);
@@ -555,7 +579,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       }
       st<bf16x4>(fin + pt_quad(jt, rho, l), cvt4(dpg));
       st<bf16x4>(fin + 8192 + pt_quad(jt, rho, l), cvt4(f));
-      ce = sum4g(ce);
+      ce = cross_row_sum(ce);
       if (g == 0) st<float>(red + 256 * rho + 4 * (16 * jt + n), ce);  // colsum(E) of these rows
     }
     // row terms: gamma_r q_r . DQ_r - gamma_r beta_r k_r . DY_r - w_r k_r . DH_r
@@ -580,8 +604,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     s3 = wave_sum(s3);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float rt = sum16(rowt[e] + erow[e]);
-      const float db = sum16(dbr[e]);
+      const float rt = row_sum16(rowt[e] + erow[e]);
+      const float db = row_sum16(dbr[e]);
       if (n == 0) {
         st<float>(red + 2048 + 4 * (16 * rho + 4 * g + e), rt);
         st<float>(red + 2304 + 4 * (16 * rho + 4 * g + e), db);

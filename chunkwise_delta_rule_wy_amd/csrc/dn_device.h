@@ -128,21 +128,38 @@ __device__ __forceinline__ void mfma_settle() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Cross-lane sums on the VALU (DPP and the gfx950 lane swaps), no LDS traffic.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp0(float x) {  // lanes without a source lane read 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+// sum over the 16 lanes of each row (every lane gets its row's sum)
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp0<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp0<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp0<0x124>(x);  // row_ror:4
+  x += dpp0<0x128>(x);  // row_ror:8
+  return x;
+}
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48]
+__device__ __forceinline__ float cross_row_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_up(x, off, 64);
-    if (l >= off) x += y;
-  }
+  x += dpp0<0x111>(x);       // row_shr:1
+  x += dpp0<0x112>(x);       // row_shr:2
+  x += dpp0<0x114>(x);       // row_shr:4
+  x += dpp0<0x118>(x);       // row_shr:8
+  x += dpp0<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+  x += dpp0<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return cross_row_sum(row_sum16(x)); }
 
 }  // namespace dn

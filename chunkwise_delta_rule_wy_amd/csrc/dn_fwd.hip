@@ -293,23 +293,23 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < LY::DMA_KQ; ++i) {
         const uint32_t dst = slot + LY::S_K + 1024 * (v + 4 * i);
-        dma16(kb_ + koff[i], dst);
-        if (WRITE_O) dma16(qb_ + koff[i], dst + LY::KQ);
+        dma16s(kb_, koff[i], dst);
+        if (WRITE_O) dma16s(qb_, koff[i], dst + LY::KQ);
       }
       if (scal) dma4(sb + soff, sdst);
 #pragma unroll
-      for (int i = 0; i < LY::DMA_V; ++i) dma16(vb_ + voff[i], slot + LY::S_V + 1024 * (v + 4 * i));
+      for (int i = 0; i < LY::DMA_V; ++i) dma16s(vb_, voff[i], slot + LY::S_V + 1024 * (v + 4 * i));
     } else {
 #pragma unroll
       for (int i = 0; i < LY::DMA_KQ; ++i) {
         const uint32_t dst = slot + LY::S_K + 1024 * (v + 4 * i);
-        if (krow[i] < Lc) dma16(kb_ + koff[i], dst);
-        if (WRITE_O && krow[i] < Lc) dma16(qb_ + koff[i], dst + LY::KQ);
+        if (krow[i] < Lc) dma16s(kb_, koff[i], dst);
+        if (WRITE_O && krow[i] < Lc) dma16s(qb_, koff[i], dst + LY::KQ);
       }
       if (scal && l < Lc) dma4(sb + soff, sdst);
 #pragma unroll
       for (int i = 0; i < LY::DMA_V; ++i)
-        if (vrow[i] < Lc) dma16(vb_ + voff[i], slot + LY::S_V + 1024 * (v + 4 * i));
+        if (vrow[i] < Lc) dma16s(vb_, voff[i], slot + LY::S_V + 1024 * (v + 4 * i));
       // rows past the end are zero (the loads never write them)
       const int tp = threadIdx.x - 4 * 64;
       for (int i = Lc * LY::RB / 16 + tp; i < LY::KQ / 16; i += 4 * 64) {

@@ -248,25 +248,25 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
 #pragma unroll
       for (int i = 0; i < LY::DMA_KQ; ++i) {
         const uint32_t dst = slot + LY::S_K + 1024 * (v + 4 * i);
-        dma16(kb_ + koff[i], dst);
-        dma16(qb_ + koff[i], dst + LY::KQ);
+        dma16s(kb_, koff[i], dst);
+        dma16s(qb_, koff[i], dst + LY::KQ);
       }
       if (scal) dma4(reinterpret_cast<const char *>(sp + r0 * H + h) + soff, sdst);
 #pragma unroll
-      for (int i = 0; i < LY::DMA_D; ++i) dma16(db_ + doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
+      for (int i = 0; i < LY::DMA_D; ++i) dma16s(db_, doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
     } else {
 #pragma unroll
       for (int i = 0; i < LY::DMA_KQ; ++i) {
         const uint32_t dst = slot + LY::S_K + 1024 * (v + 4 * i);
         if (krow[i] < Lc) {
-          dma16(kb_ + koff[i], dst);
-          dma16(qb_ + koff[i], dst + LY::KQ);
+          dma16s(kb_, koff[i], dst);
+          dma16s(qb_, koff[i], dst + LY::KQ);
         }
       }
       if (scal && l < Lc) dma4(reinterpret_cast<const char *>(sp + r0 * H + h) + soff, sdst);
 #pragma unroll
       for (int i = 0; i < LY::DMA_D; ++i)
-        if (drow[i] < Lc) dma16(db_ + doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
+        if (drow[i] < Lc) dma16s(db_, doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
       // rows past the end are zero (the loads never write them)
       const int tp = threadIdx.x - 4 * 64;
       for (int i = Lc * LY::RB / 16 + tp; i < LY::KQ / 16; i += 4 * 64) {

@@ -416,9 +416,12 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     float x[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = (4 * qr + k == c) ? 1.f : 0.f;
+    f32x4 acol[15];  // every column first: the chain below then waits on no LDS read
+#pragma unroll
+    for (int j = 0; j < 15; ++j) acol[j] = ld<f32x4>(priv + 96 * j + 16 * qr);
 #pragma unroll
     for (int j = 0; j < 15; ++j) {
-      const f32x4 a = ld<f32x4>(priv + 96 * j + 16 * qr);
+      const f32x4 a = acol[j];
       const float own = x[j & 3];
       const float xj = (j >> 2) == 0 ? quad_bcast<0>(own)
                      : (j >> 2) == 1 ? quad_bcast<1>(own)

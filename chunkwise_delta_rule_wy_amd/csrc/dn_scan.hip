@@ -233,7 +233,9 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
   // chunk of order o (o = 0 is the last chunk) and its ring slot
   auto chunk_of = [&](int o) { return nch - 1 - o; };
   auto slot_of = [&](int o) { return sbase + (uint32_t)(o % NBUF) * LY::SLOT; };
-  auto issue = [&](int o) {
+  // loads of order o in four parts issued between the prep stages (K, g and
+  // beta; K; Q; dO: dO last); a partial chunk loads everything in part 0
+  auto issue = [&](int o, int part) {
     const int cc = chunk_of(o);
     const uint32_t slot = slot_of(o);
     const int Lc = min(CH, si.len - cc * CH);
@@ -245,16 +247,22 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
     const bool scal = (v == 1) || (GATED && v == 0);
     const uint32_t sdst = slot + (v == 0 ? LY::S_G : LY::S_BETA);
     if (Lc == CH) {
+      constexpr int KH = (LY::DMA_KQ + 1) / 2;
+      if (part == 0) {
 #pragma unroll
-      for (int i = 0; i < LY::DMA_KQ; ++i) {
-        const uint32_t dst = slot + LY::S_K + 1024 * (v + 4 * i);
-        dma16s(kb_, koff[i], dst);
-        dma16s(qb_, koff[i], dst + LY::KQ);
+        for (int i = 0; i < KH; ++i) dma16s(kb_, koff[i], slot + LY::S_K + 1024 * (v + 4 * i));
+        if (scal) dma4(reinterpret_cast<const char *>(sp + r0 * H + h) + soff, sdst);
+      } else if (part == 1) {
+#pragma unroll
+        for (int i = KH; i < LY::DMA_KQ; ++i) dma16s(kb_, koff[i], slot + LY::S_K + 1024 * (v + 4 * i));
+      } else if (part == 2) {
+#pragma unroll
+        for (int i = 0; i < LY::DMA_KQ; ++i) dma16s(qb_, koff[i], slot + LY::S_Q + 1024 * (v + 4 * i));
+      } else {
+#pragma unroll
+        for (int i = 0; i < LY::DMA_D; ++i) dma16s(db_, doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
       }
-      if (scal) dma4(reinterpret_cast<const char *>(sp + r0 * H + h) + soff, sdst);
-#pragma unroll
-      for (int i = 0; i < LY::DMA_D; ++i) dma16s(db_, doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
-    } else {
+    } else if (part == 0) {
 #pragma unroll
       for (int i = 0; i < LY::DMA_KQ; ++i) {
         const uint32_t dst = slot + LY::S_K + 1024 * (v + 4 * i);
@@ -297,7 +305,8 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
   const int cg0 = p.chunk_base ? p.chunk_base[n_seq] : n_seq * p.NC;
 
   if (!chain) {
-    if (nch > 0) issue(0);
+    if (nch > 0)
+      for (int part = 0; part < 4; ++part) issue(0, part);
     wait_vm<0>();
   }
   __syncthreads();
@@ -312,7 +321,10 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
         chain_chunk<DK, GATED>(lb, hs, slot_of(s), ob, dtr, dpr, dst);
       }
     } else {
-      if (s + 2 < nch) issue(s + 2);
+      const bool iss_now = s + 2 < nch;
+      auto iss = [&](int part) {
+        if (iss_now) issue(s + 2, part);
+      };
       const int o = s + 1;
       if (o < nch) {
         const int c = chunk_of(o);
@@ -322,10 +334,10 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
         const int L = min(CH, si.len - c * CH);
         const ScanKsw<DK> ksw{lb.frag};
         const uint32_t ka = slot + LY::S_K, qa = slot + LY::S_Q, ga = slot + LY::S_G, ba = slot + LY::S_BETA;
-        if (v == 0) prep_chunk<DK, GATED, true, MODE_SCAN, 0>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw);
-        else if (v == 1) prep_chunk<DK, GATED, true, MODE_SCAN, 1>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw);
-        else if (v == 2) prep_chunk<DK, GATED, true, MODE_SCAN, 2>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw);
-        else prep_chunk<DK, GATED, true, MODE_SCAN, 3>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw);
+        if (v == 0) prep_chunk<DK, GATED, true, MODE_SCAN, 0>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        else if (v == 1) prep_chunk<DK, GATED, true, MODE_SCAN, 1>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        else if (v == 2) prep_chunk<DK, GATED, true, MODE_SCAN, 2>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        else prep_chunk<DK, GATED, true, MODE_SCAN, 3>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
       }
       // K, Q, g, beta of order s + 2 (and everything older) land before the
       // barrier; its dO may stay in flight until the next one

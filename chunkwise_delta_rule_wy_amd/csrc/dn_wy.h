@@ -212,6 +212,13 @@ __device__ __forceinline__ uint32_t pt_frag(int t, int kb, int l) {
 }
 __device__ __forceinline__ constexpr int m_block(int i, int j) { return i * (i - 1) / 2 + j; }
 
+// Hook that lets a prep wave issue the direct loads of a later chunk between
+// the stages of a preparation, so that the vector-memory path works while the
+// wave computes instead of stalling it up front (stages 0..3).
+struct NoIssue {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 using I0 = std::integral_constant<int, 0>;
 using I1 = std::integral_constant<int, 1>;
 using I2 = std::integral_constant<int, 2>;
@@ -233,10 +240,10 @@ using I3 = std::integral_constant<int, 3>;
 // M_vv^T and the plain gate table, the scan one the gate table of the scaled
 // state gradient.  kbase, qbase: K and Q tiles (K-tile swizzle KSW); gaddr, baddr:
 // g and beta of the chunk's rows (fp32, LDS); rows >= L are padding.
-template <int DK, bool GATED, bool WRITE_P, int MODE, int PW, typename KSW>
+template <int DK, bool GATED, bool WRITE_P, int MODE, int PW, typename KSW, typename ISS = NoIssue>
 __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint32_t qbase, uint32_t gaddr,
                                            uint32_t baddr, uint32_t ob, uint32_t priv, int L, float &scale,
-                                           KSW ksw) {
+                                           KSW ksw, ISS iss = ISS{}) {
   using RS = Res<MODE>;
   constexpr bool BWD = MODE != MODE_FWD;
   constexpr int KB = DK / 32;
@@ -283,6 +290,7 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     }
     wave_lds_fence();
   }
+  iss(0);
 
   bf16x8 kf[4][KB];  // K rows 16t + n, d_k block kb
 #pragma unroll
@@ -317,6 +325,8 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     if constexpr (MODE == MODE_CHUNK) st<bf16x4>(ob + RS::O_M + 512 * (6 + PW) + lb.m, cvt4(mv));  // M_vv^T row n
   }
 
+  iss(1);
+
   // Block (TI, TJ) of -M below the diagonal: lane (n, g) holds k_r . k_j with
   // r = 16TI + n, j = 16TJ + 4g + e.
   auto mtile = [&](auto ti_c, auto tj_c) {
@@ -343,6 +353,8 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     mtile(I3{}, I1{});
     mtile(I3{}, I2{});
   }
+
+  iss(2);
 
   if constexpr (WRITE_P) {
     // P block (TI, TJ), TJ <= TI.  Forward: lane (n, g) holds q_r . k_j with
@@ -406,6 +418,8 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
       ptile(I3{}, I2{}, qa);
     }
   }
+
+  iss(3);
 
   // (I + A_vv)^-1 (times diag(beta) in the forward variant): lane (c, qr) =
   // (l / 4, l % 4) holds rows 4qr .. 4qr + 3 of column c; column j of A_vv is

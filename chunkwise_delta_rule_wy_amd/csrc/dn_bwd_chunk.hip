@@ -72,7 +72,7 @@ __device__ __forceinline__ int swz_s(int r) {  // K, Q, S, dS (rows of 2 d_k byt
 }
 __device__ __forceinline__ int swz_v32(int r) { return ((r >> 2) & 1) << 1; }  // V tile, 64-byte rows
 __device__ __forceinline__ int swz_d32(int r) { return ((r >> 3) & 1) << 1; }  // dO tile, 64-byte rows
-__device__ __forceinline__ int swz_x(int r) { return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2); }
+__device__ __forceinline__ int swz_xn(int r) { return (((r >> 2) & 1) << 1) ^ (((r >> 3) & 1) * 3); }  // V', Y hand-over
 
 template <int DK>
 struct BLay {
@@ -83,7 +83,7 @@ struct BLay {
   static constexpr int O_RES = 2 * KQ;         // prep results (the gate table holds beta too)
   static constexpr int O_BETA = O_RES + RS::BYTES;  // beta (0 past the end)
   static constexpr int O_X = O_BETA + 256;     // two hand-over buffers; the prep scratch and g, beta before
-  static constexpr int XB = 8192;              // V'^T (32 x 64 bf16) then Y^T
+  static constexpr int XB = 8192;              // V' then Y, [64 tokens][32 columns] bf16 each
   static constexpr int O_XG = O_X + 4 * PRIV_BYTES;  // direct-load targets of g and beta
   static constexpr int O_XB = O_XG + 256;
   static constexpr int O_T = O_X + 2 * XB;     // ring of tile buffers: V, dO (64 x 32), S, dS (32 x d_k)
@@ -149,17 +149,9 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     const int r = 8 * g + 4 * hh + e4, s = swz_s<DK>(r);
     lb_str[hh] = r * RB + 8 * q4 + 32 * (s >> 1);
   }
-  uint32_t lb_xw;  // V'^T / Y^T row n, tokens 16i + 4g: lb_xw ^ 32 i
-  {
-    const int s = swz_x(n);
-    lb_xw = n * 128 + 32 * (s >> 1) + 16 * ((g >> 1) ^ (s & 1)) + 8 * (g & 1);
-  }
-  uint32_t lb_xtr[2];  // V'^T / Y^T transposed reads: rows 8g + 4hh + e, tokens 16jt + 4q
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int r = 8 * g + 4 * hh + e4, s = swz_x(r);
-    lb_xtr[hh] = r * 128 + 32 * (s >> 1) + 16 * ((q4 >> 1) ^ (s & 1)) + 8 * (q4 & 1);
-  }
+  // hand-over buffers (V', Y as [token][column], 64-byte rows): fragment
+  // reads, lane (n, g): row 16j + n, columns 8g .. 8g + 7 at 1024 j + lb_xf
+  const uint32_t lb_xf = n * 64 + 16 * (g ^ swz_xn(n));
   const uint32_t lb_m = 32 * n + ((8 * g) ^ (16 * ((n >> 3) & 1)));           // 16x16 block row reads
   const int rb4 = 4 * g + e4;
   const uint32_t lb_btr = 32 * rb4 + ((8 * q4) ^ (16 * ((rb4 >> 3) & 1)));  // 16x16 block transposed reads
@@ -319,20 +311,23 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m <= i; ++m)
           ra[i * (i + 1) / 2 + m] = ld_tr((m == i ? ob + RS::O_TT + 512 * i : rbuf + 512 * m_block(i, m)) + lb_btr);
-      uint32_t lb_vtr;  // V transposed reads: rows 16t + 4g + e, columns 16cs + 4q
+      uint32_t lb_vtr, lb_ytr, lb_xw;
       {
-        const int r = 4 * g + e4;
+        const int r = 4 * g + e4;  // V and Y transposed reads: rows 16t + 4g + e, columns 16cs + 4q
         lb_vtr = r * 64 + 16 * ((2 * cs + (q4 >> 1)) ^ swz_v32(r)) + 8 * (q4 & 1);
+        lb_ytr = r * 64 + 16 * ((2 * cs + (q4 >> 1)) ^ swz_xn(r)) + 8 * (q4 & 1);
+        // V' writes, lane (n, g): row 16i + n, columns 16cs + 4g .. + 3 at 1024 i + lb_xw
+        lb_xw = n * 64 + 16 * ((2 * cs + (g >> 1)) ^ swz_xn(n)) + 8 * (g & 1);
       }
       f32x4 xp[4], xy[4];  // X of the previous tile; rowsum(X * Y) partials (rows 16i + 4g + e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) xp[i] = xy[i] = zero4();
       for (int s = 0; s <= ntiles; ++s) {
-        if (s > 0) {  // rowsum(X * Y) of tile s - 1 (Y^T handed over by the B wave)
-          const uint32_t yb = xbuf(s - 1) + 4096 + 16 * cs * 128;
+        if (s > 0) {  // rowsum(X * Y) of tile s - 1 (Y handed over by the B wave)
+          const uint32_t yb = xbuf(s - 1) + 4096;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bf16x4 yv = ld<bf16x4>(yb + (lb_xw ^ (32 * i)));
+            const bf16x4 yv = ld_tr(yb + 1024 * i + lb_ytr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) xy[i][e] += xp[i][e] * bf2f(yv[e]);
           }
@@ -352,20 +347,19 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) xp[t][e] = bf2f(vr[e]) - gm[e] * yk[e];
           }
-          // V' = R diag(beta) X: V'_i = sum_{m<=i} R_im (beta_m X_m)
-          bf16x4 bx[4], vb[4];
+          // V' = R diag(beta) X, as V'_i^T = sum_{m<=i} (beta_m X_m)^T R_im^T so
+          // that lane (n, g) holds columns 4g .. 4g + 3 of token 16i + n
+          bf16x4 bx[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m) bx[m] = cvt4(xp[m] * bet4(m));
+          const uint32_t xv = xbuf(s);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 0; m <= i; ++m) acc = mma16(acc, ra[i * (i + 1) / 2 + m], bx[m]);
-            vb[i] = cvt4(acc);
+            for (int m = 0; m <= i; ++m) acc = mma16(acc, bx[m], ra[i * (i + 1) / 2 + m]);
+            st<bf16x4>(xv + 1024 * i + lb_xw, cvt4(acc));
           }
-          const uint32_t xv = xbuf(s) + 16 * cs * 128;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st<bf16x4>(xv + (lb_xw ^ (32 * i)), vb[i]);
         }
         mfma_settle();
         __syncthreads();
@@ -393,6 +387,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i <= m; ++i)
           rb[m * (m + 1) / 2 + i] = ld<bf16x4>((m == i ? ob + RS::O_TT + 512 * i : rbuf + 512 * m_block(m, i)) + lb_m);
+      // Y writes, lane (n, g): row 16i + n, columns 16cs + 4g .. + 3 at 1024 i + lb_xw
+      const uint32_t lb_xw = n * 64 + 16 * ((2 * cs + (g >> 1)) ^ swz_xn(n)) + 8 * (g & 1);
       uint32_t lb_dtr[2];  // dO transposed reads, rows 8g + 4hh + e (+ 32 kb), columns 16cs + 4q
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -422,28 +418,23 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           dvp[1] = mma32(mma32(dvp[1], ptf[2], dob[0]), ptf[3], dob[1]);
           dvp[2] = mma32(dvp[2], ptf[4], dob[1]);
           dvp[3] = mma32(dvp[3], ptf[5], dob[1]);
-          // Y = R^T dV': Y_i = sum_{m>=i} (R_mi)^T dV'_m;  dX = diag(beta) Y
+          // Y = R^T dV', as Y_i^T = sum_{m>=i} dV'_m^T R_mi so that lane (n, g)
+          // holds columns 4g .. 4g + 3 of token 16i + n;  dX = diag(beta) Y = dv
           bf16x4 db16[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m) db16[m] = cvt4(dvp[m]);
-          f32x4 y[4];
-          float *dvb = p.dv + (row0 * H + h) * (size_t)DV + TC * s;  // wave-uniform
+          float *dvb = p.dv + (row0 * H + h) * (size_t)DV + TC * s + 16 * cs + 4 * g;  // + token row
+          const uint32_t yb = xbuf(s) + 4096;
 #pragma unroll
           for (int i = 3; i >= 0; --i) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 3; m >= i; --m) acc = mma16(acc, rb[m * (m + 1) / 2 + i], db16[m]);
-            y[i] = acc;
-            const f32x4 dx = y[i] * bet4(i);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 16 * i + 4 * g + e;
-              if (r < L) dvb[(uint32_t)(r * H * DV + 16 * cs + n)] = dx[e];
-            }
+            for (int m = 3; m >= i; --m) acc = mma16(acc, db16[m], rb[m * (m + 1) / 2 + i]);
+            st<bf16x4>(yb + 1024 * i + lb_xw, cvt4(acc));
+            const int r = 16 * i + n;
+            if (r < L)
+              *reinterpret_cast<f32x4 *>(dvb + (uint32_t)(r * H * DV)) = acc * ld<float>(sb + LY::O_BETA + 4 * r);
           }
-          const uint32_t yb = xbuf(s) + 4096 + 16 * cs * 128;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st<bf16x4>(yb + (lb_xw ^ (32 * i)), cvt4(y[i]));
         }
         mfma_settle();
         __syncthreads();
@@ -451,7 +442,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     }
     __syncthreads();  // dPG^T, F^T and the reductions are complete
 
-    // dk (column part) of token rows 16w + 4g + e: dPG^T Q + F^T K
+    // dk (column part) of token rows 16w .. 16w + 15: dPG^T Q + F^T K
     {
       bf16x8 pgt[2], ft[2];
 #pragma unroll
@@ -467,8 +458,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
           const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
           const bf16x8 qt = cat(ld_tr(sb + LY::O_Q + a0), ld_tr(sb + LY::O_Q + a1));
-          dk = mma32(dk, pgt[kb], qt);
-          dk = mma32(dk, ft[kb], kt);
+          dk = mma32(dk, qt, pgt[kb]);  // (dPG^T Q + F^T K)^T: lane (n, g) row 16w + n, columns 16mt + 4g ..
+          dk = mma32(dk, kt, ft[kb]);
         }
         st<f32x4>(dkx + 16 * ((w * MT + mt) * 64 + l), dk);
       }
@@ -480,7 +471,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) ce += ld<float>(red + 256 * ww + 4 * r);
       const float xyr = ld<float>(red + 1024 + 4 * r) + ld<float>(red + 1280 + 4 * r);
-      float db = ld<float>(red + 2048 + 4 * r) - ce;
+      float db = ld<float>(red + 2048 + 4 * r) + ld<float>(red + 2816 + 4 * r) - ce;
       if (r == CH - 1) {
         float s3t = 0.f;
 #pragma unroll
@@ -503,6 +494,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     const int rho = w == 4 ? 3 : w == 5 ? 0 : w == 6 ? 2 : 1;  // token rows 16rho .. 16rho + 15
     const bool hdh_wave = rho == 0;
     const uint32_t lb_dfrag = (16 * rho + n) * 64 + 16 * (g ^ swz_d32(n));  // dO frag, row 16rho + n
+    // dP, dA: lane (n, g) holds rows 16rho + 4g + e, column 16jt + n;
+    // dq1 = dO h^T, dk1 = Y h^T, dk2 = V' dh^T: row 16rho + n, columns 16mt + 4g + e
     f32x4 dP[4], dAc[4], dq1[MT], dk1[MT], dk2[MT];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dP[t] = dAc[t] = zero4();
@@ -515,12 +508,13 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         const int j = s - 1;
         const uint32_t tb = tbuf(j), xv = xbuf(j), xyb = xbuf(j) + 4096;
         const bf16x8 dof = ld<bf16x8>(tb + LY::T_DO + lb_dfrag);
-        const bf16x8 yf = cat(ld_tr(xyb + (lb_xtr[0] ^ (32 * rho))), ld_tr(xyb + (lb_xtr[1] ^ (32 * rho))));
-        const bf16x8 vf = cat(ld_tr(xv + (lb_xtr[0] ^ (32 * rho))), ld_tr(xv + (lb_xtr[1] ^ (32 * rho))));
+        const bf16x8 yf = ld<bf16x8>(xyb + 1024 * rho + lb_xf);
         // every token block: the blocks above the diagonal (jt > rho) are masked in the final phase
+        bf16x8 vf;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          const bf16x8 vt = cat(ld_tr(xv + (lb_xtr[0] ^ (32 * jt))), ld_tr(xv + (lb_xtr[1] ^ (32 * jt))));
+          const bf16x8 vt = ld<bf16x8>(xv + 1024 * jt + lb_xf);
+          if (jt == rho) vf = vt;
           dP[jt] = mma32(dP[jt], dof, vt);
           dAc[jt] = mma32(dAc[jt], yf, vt);
         }
@@ -529,9 +523,9 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           const uint32_t a0 = lb_str[0] ^ (32 * mt), a1 = lb_str[1] ^ (32 * mt);
           const bf16x8 sf = cat(ld_tr(tb + LY::T_S + a0), ld_tr(tb + LY::T_S + a1));
           const bf16x8 dsf = cat(ld_tr(tb + LY::T_DS + a0), ld_tr(tb + LY::T_DS + a1));
-          dq1[mt] = mma32(dq1[mt], dof, sf);
-          dk1[mt] = mma32(dk1[mt], yf, sf);
-          dk2[mt] = mma32(dk2[mt], vf, dsf);
+          dq1[mt] = mma32(dq1[mt], sf, dof);
+          dk1[mt] = mma32(dk1[mt], sf, yf);
+          dk2[mt] = mma32(dk2[mt], dsf, vf);
           if (hdh_wave) hdh = dot8(sf, dsf, hdh);
         }
       }
@@ -543,7 +537,9 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     }
 
     // ---- final phase (row wave rho: rows r = 16rho + 4g + e)
-    const f32x4 gam_r = gam4(rho), w_r = w4(rho), bet_r = bet4(rho);
+    const f32x4 bet_r = bet4(rho);
+    float *const dqb = p.dq + ((row0 + 16 * rho) * H + h) * (size_t)DK;  // rows of this block (wave-uniform)
+    float *const dkb = p.dk + ((row0 + 16 * rho) * H + h) * (size_t)DK;
     const f32x4 bl_r = GATED ? ld<f32x4>(cgt + CG_BL + 4 * (16 * rho + 4 * g)) : zero4();
     f32x4 erow = zero4(), dbr = zero4();
 #pragma unroll
@@ -583,31 +579,35 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       if (g == 0) st<float>(red + 256 * rho + 4 * (16 * jt + n), ce);  // colsum(E) of these rows
     }
     // row terms: gamma_r q_r . DQ_r - gamma_r beta_r k_r . DY_r - w_r k_r . DH_r
-    uint32_t lb_rtr;  // K, Q transposed reads: rows 16rho + 4g + e, columns 16mt + 4q
-    {
-      const int r = 4 * g + e4, s = swz_s<DK>(r);
-      lb_rtr = (16 * rho + r) * RB + 8 * q4 + 32 * (s >> 1);
-    }
-    f32x4 rowt = zero4();
-    float s3 = 0.f;
+    // (lane (n, g): token row r = 16rho + n, d_k columns 16mt + 4g .. + 3)
+    const int rr = 16 * rho + n;
+    const float gam_n = GATED ? ld<float>(cgt + CG_GS + 4 * rr) : 1.f;
+    const float w_n = GATED ? ld<float>(cgt + CG_WS + 4 * rr) : 1.f;
+    const float bet_n = ld<float>(sb + LY::O_BETA + 4 * rr);
+    const uint32_t lb_qr = rr * RB + 8 * (g & 1);  // Q, K row rr, columns 16mt + 4g: + 16 ((2mt + g/2) ^ swz)
+    const int sq = swz_s<DK>(n);
+    float rowq = 0.f, rowk = 0.f, s3 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const bf16x4 qv = ld_tr(sb + LY::O_Q + (lb_rtr ^ (32 * mt)));
-      const bf16x4 kv = ld_tr(sb + LY::O_K + (lb_rtr ^ (32 * mt)));
+      const uint32_t a = lb_qr + 16 * ((2 * mt + (g >> 1)) ^ sq);
+      const bf16x4 qv = ld<bf16x4>(sb + LY::O_Q + a);
+      const bf16x4 kv = ld<bf16x4>(sb + LY::O_K + a);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float kdh = bf2f(kv[e]) * dk2[mt][e];
-        rowt[e] += gam_r[e] * (bf2f(qv[e]) * dq1[mt][e] - bet_r[e] * bf2f(kv[e]) * dk1[mt][e]) - w_r[e] * kdh;
-        s3 += w_r[e] * kdh;
+        rowq += bf2f(qv[e]) * dq1[mt][e];
+        rowk += bf2f(kv[e]) * (bet_n * gam_n * dk1[mt][e] + w_n * dk2[mt][e]);
+        s3 += bf2f(kv[e]) * dk2[mt][e];
       }
     }
-    s3 = wave_sum(s3);
+    const float rt = cross_row_sum(gam_n * rowq - rowk);  // over the lane groups: all of d_k
+    s3 = wave_sum(w_n * s3);
+    if (g == 0) st<float>(red + 2048 + 4 * rr, rt);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float rt = row_sum16(rowt[e] + erow[e]);
+      const float er = row_sum16(erow[e]);
       const float db = row_sum16(dbr[e]);
       if (n == 0) {
-        st<float>(red + 2048 + 4 * (16 * rho + 4 * g + e), rt);
+        st<float>(red + 2816 + 4 * (16 * rho + 4 * g + e), er);
         st<float>(red + 2304 + 4 * (16 * rho + 4 * g + e), db);
       }
     }
@@ -619,10 +619,12 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     mfma_settle();
     __syncthreads();  // dPG^T, F^T and the reductions are complete
 
-    // dq = diag(gamma) dO h^T + dPG K ;  dk (row part) = diag(w) V' dh^T - diag(gamma beta) Y h^T + F K
+    // dq = diag(gamma) dO h^T + dPG K ;  dk (row part) = diag(w) V' dh^T - diag(gamma beta) Y h^T + F K,
+    // as dq^T = gamma dq1^T + K^T dPG^T (and likewise dk): lane (n, g) holds row r = 16rho + n,
+    // columns 16mt + 4g .. + 3, written as one 16-byte store
     f32x4 dkr[MT];
     {
-      bf16x8 pgr[2], fr[2];  // A operands: rows r of dPG and F, read transposed from dPG^T, F^T
+      bf16x8 pgr[2], fr[2];  // B operands: rows r of dPG and F, read transposed from dPG^T, F^T
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int r0 = 32 * kb + 8 * g + e4, r1 = r0 + 4;  // dPG^T rows j
@@ -634,21 +636,17 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4 dq = gam_r * dq1[mt];
-        f32x4 dk = w_r * dk2[mt] - gam_r * bet_r * dk1[mt];
+        f32x4 dq = gam_n * dq1[mt];
+        f32x4 dk = w_n * dk2[mt] - (gam_n * bet_n) * dk1[mt];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
           const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
-          dq = mma32(dq, pgr[kb], kt);
-          dk = mma32(dk, fr[kb], kt);
+          dq = mma32(dq, kt, pgr[kb]);
+          dk = mma32(dk, kt, fr[kb]);
         }
         dkr[mt] = dk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rho + 4 * g + e;
-          if (r < L) p.dq[((row0 + r) * H + h) * (size_t)DK + 16 * mt + n] = dq[e];
-        }
+        if (rr < L) *reinterpret_cast<f32x4 *>(dqb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dq;
       }
     }
     mfma_settle();
@@ -656,11 +654,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const f32x4 dk = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rho + 4 * g + e;
-        if (r < L) p.dk[((row0 + r) * H + h) * (size_t)DK + 16 * mt + n] = dk[e];
-      }
+      if (rr < L) *reinterpret_cast<f32x4 *>(dkb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dk;
     }
   }
 }

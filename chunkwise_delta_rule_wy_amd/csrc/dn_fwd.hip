@@ -114,13 +114,6 @@ __device__ __forceinline__ void chain_chunk(const FwdParams &p, const Bases &lb,
   const int l = lane_id(), n = l & 15, g = l >> 4;
   const int H = p.H, DV = p.DV;
 
-  if constexpr (STORE_STATES) {  // the state at the chunk start, h = s_c h~, as S = h^T in bf16
-    const float sc = GATED ? ld<float>(ob + LY::O_CG + CG_SC) : 1.f;
-    bf16 *dst = states_dst + (size_t)col * DK + 8 * g;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      *reinterpret_cast<bf16x8 *>(dst + 32 * kb) = bfrag<bf16>(hs[2 * kb] * sc, hs[2 * kb + 1] * sc);
-  }
   bf16x8 hb[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) hb[kb] = bfrag<bf16>(hs[2 * kb], hs[2 * kb + 1]);
@@ -192,6 +185,16 @@ __device__ __forceinline__ void chain_chunk(const FwdParams &p, const Bases &lb,
         acc = mma32(acc, cat(vb[2 * kb], vb[2 * kb + 1]), ld<bf16x8>(ob + LY::O_P + p_read(lb, nt, kb)));
       if (16 * nt + n < L) *reinterpret_cast<bf16x4 *>(orow + (size_t)(16 * nt + n) * H * DV) = cvt4(acc);
     }
+  }
+  // the state at the chunk start, h = s_c h~, as S = h^T in bf16: stored here,
+  // late in the step, so that the stores do not compete with the prep waves'
+  // loads, which are issued at the start of the step
+  if constexpr (STORE_STATES) {
+    const float sc = GATED ? ld<float>(ob + LY::O_CG + CG_SC) : 1.f;
+    bf16 *dst = states_dst + (size_t)col * DK + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      *reinterpret_cast<bf16x8 *>(dst + 32 * kb) = bfrag<bf16>(hs[2 * kb] * sc, hs[2 * kb + 1] * sc);
   }
   // h~ <- h~ + K^T diag(w / s_{c+1}) V'   (after h~ *= gamma_63 s_c on a rescale)
   bf16x8 wb[2];

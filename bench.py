@@ -27,6 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+# HBM bytes per launch of the chunk-gradient kernel at workload 4, from rocprofv3
+# FETCH_SIZE and WRITE_SIZE scaled by what the same counters read for a copy of
+# known size (commands and raw counts under profiles/); it describes the kernel as
+# built when the counters were taken
+CHUNK_GRAD_TRAFFIC_W4 = 1511.2e6
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
 
 
@@ -157,8 +162,9 @@ def main():
     else:
         kname, kus, kbytes = "dn::fwd_bf16_kernel", stage_us["fwd"], workload_bytes(sh, False)
     achieved = kbytes / (kus * 1e-6) / 1e9
+    traffic = CHUNK_GRAD_TRAFFIC_W4 if (backward and wid == 4) else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kname, "kernel_us": round(kus, 2), "bytes_per_launch": kbytes}
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
 

@@ -5,7 +5,8 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 A step is one pass of the hot path over one batch of seeded synthetic input
 already resident in HBM: for the default workload (gated delta rule, bf16,
 B=4 T=4096 H=16 dk=128 dv=256) that is the chunkwise forward pass plus the
-chunkwise backward pass (dq, dk, dv, dbeta, dg, dh0).  Workloads 2, 3 and 5
+chunkwise backward pass (dq, dk, dv, dbeta, dg, dh0); workload 6 is the same for
+the packed varlen input of workload 5.  Workloads 2, 3 and 5
 are forward-only; "dec" is one decode step at batch 256, H=32, d=128.
 
 Prints one JSON line: tokens/s and algorithmic TFLOP/s (with the fraction of
@@ -222,6 +223,8 @@ def cpu_baseline(x, sh, backward, budget_s):
         oracle.fwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, nthreads=nthr)
         if backward:
             dO = sel(x["dO"])
+            if sh.lengths is not None:
+                dO = dO[:, :T]
             dhT = torch.stack([x["dhT"][b, h] for b, h in zip(b_idx, h_idx)]).unsqueeze(1)
             oracle.bwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, dO, dhT, nthreads=nthr)
         elapsed = time.perf_counter() - t0

@@ -237,12 +237,11 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   issue_kq();
   if (w >= 4) {
     issue_tile(0);
-    if (ntiles > 1) {
-      issue_tile(1);
-      if (full) wait_vm<LY::DMA_T>(); else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
+    if (ntiles > 1) issue_tile(1);
+    // K, Q, g, beta land before the prep; the tiles stay in flight through it
+    if (!full) wait_vm<0>();
+    else if (ntiles > 1) wait_vm<2 * LY::DMA_T>();
+    else wait_vm<LY::DMA_T>();
   } else {
     wait_vm<0>();
   }
@@ -289,6 +288,11 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   if (w == 4) rcol(I0{});
   else if (w == 5) rcol(I1{});
   else if (w == 6) rcol(I2{});
+  // tile 0 lands before the pipeline starts; tile 1 may stay in flight
+  if (w >= 4) {
+    if (full && ntiles > 1) wait_vm<LY::DMA_T>();
+    else wait_vm<0>();
+  }
   __syncthreads();
 
   const uint32_t red = sb + LY::O_RED, fin = sb + LY::O_FIN, dkx = sb + LY::O_DKX;

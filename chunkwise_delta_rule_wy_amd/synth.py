@@ -22,6 +22,7 @@ id    shape                                                        dtype
 3     B=4  T=4096  H=16 dk=128 dv=256, gated, h0                   bf16
 4     workload 3 plus dO, dhT (forward + backward)                 bf16
 5     varlen: 8 packed sequences, 65536 tokens, H=32, dk=dv=128    bf16
+6     workload 5 plus dO, dhT (forward + backward, packed)         bf16
 5dec  decode: batch 256, H=32, dk=dv=128, state fp32                bf16
 ====  ==========================================================  ========
 """
@@ -71,6 +72,8 @@ WORKLOADS = {
              backward=True),
     5: Shape(1, 65536, 32, 128, 128, torch.bfloat16, gated=True, has_h0=True,
              lengths=VARLEN_LENGTHS),
+    6: Shape(1, 65536, 32, 128, 128, torch.bfloat16, gated=True, has_h0=True,
+             backward=True, lengths=VARLEN_LENGTHS),
 }
 
 WORKLOAD_NAMES = {
@@ -79,6 +82,7 @@ WORKLOAD_NAMES = {
     3: "gated-bf16-B4-T4096-H16-dk128-dv256",
     4: "gated-fwd+bwd-bf16-B4-T4096-H16-dk128-dv256",
     5: "varlen-gated-bf16-8seqs-65536tok-H32-d128",
+    6: "varlen-gated-fwd+bwd-bf16-8seqs-65536tok-H32-d128",
 }
 
 

@@ -6,7 +6,9 @@ its Python binding) never touches it, and the two share no code: this wraps
 ``dn_oracle.c``, a plain token-by-token recurrence in double precision
 (Gated DeltaNet review thread, Table 1, rows "DeltaNet" / "Gated DeltaNet":
 S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t),
-its sequential adjoint, and a single recurrent step.
+its sequential adjoint, and a single recurrent step; and the Longhorn row of
+the same table (the delta rule at the step size beta / (1 + beta |k|^2)),
+with its gradient by the chain rule through that step size.
 
 Inputs may be torch tensors (any float dtype, on any device) or numpy arrays;
 they are upcast exactly to float64 on the host.  Results are float64 numpy.
@@ -137,3 +139,43 @@ def step(q, k, v, beta, g, state, nthreads=0):
     if rc:
         raise ValueError("oracle_step failed (%d)" % rc)
     return o, st
+
+
+# ------------------------------------------------------------------ Longhorn
+# Gated DeltaNet review thread, Table 1, row "Longhorn" (with the scalar beta
+# of the table's caption): the delta-rule update with the step size
+#     eps_t = beta_t / (1 + beta_t k_t^T k_t)
+# in place of beta_t, S_t = S_{t-1}(I - eps_t k_t k_t^T) + eps_t v_t k_t^T.
+# The row has no decay; g is passed through to the recurrence unchanged.
+
+def longhorn_eps(k, beta):
+    """eps = beta / (1 + beta |k|^2) per (token, head), float64 [..., H]."""
+    k, beta = _f64(k), _f64(beta)
+    return beta / (1.0 + beta * np.sum(k * k, axis=-1))
+
+
+def longhorn_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, nthreads=0):
+    """Forward pass of the Longhorn recurrence: (o, hT) as float64."""
+    return fwd(q, k, v, longhorn_eps(k, beta), g, h0, cu_seqlens, nthreads)
+
+
+def longhorn_eps_bwd(k, beta, deps):
+    """Chain rule through eps = beta / (1 + beta s), s = |k|^2:
+    dbeta = deps / (1 + beta s)^2 and the extra key gradient
+    deps * (-beta^2 / (1 + beta s)^2) * 2 k.  Returns (dbeta, dk_extra)."""
+    k, beta, deps = _f64(k), _f64(beta), _f64(deps)
+    den = 1.0 + beta * np.sum(k * k, axis=-1)
+    dbeta = deps / (den * den)
+    dk = (deps * (-2.0 * beta * beta / (den * den)))[..., None] * k
+    return dbeta, dk
+
+
+def longhorn_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, nthreads=0):
+    """Backward pass of <dO, o> + <dhT, hT> for the Longhorn recurrence: the
+    delta-rule adjoint at beta = eps, then the chain rule through eps."""
+    eps = longhorn_eps(k, beta)
+    gr = bwd(q, k, v, eps, g, h0, dO, dhT, cu_seqlens, nthreads)
+    dbeta, dk_extra = longhorn_eps_bwd(k, beta, gr["dbeta"])
+    gr["dbeta"] = dbeta
+    gr["dk"] = gr["dk"] + dk_extra
+    return gr

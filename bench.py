@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--workload", default="4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--variant", choices=("delta", "longhorn"), default="delta",
+                    help="longhorn: the step size eps = beta / (1 + beta |k|^2) of Table 1's "
+                         "Longhorn row, computed (and differentiated) around the same passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -128,15 +131,27 @@ def main():
     fev = [(mk(), mk()) for _ in range(nev)]
     bev = [[mk() for _ in range(4)] for _ in range(nev)] if backward else None
 
+    longhorn = args.variant == "longhorn"
+    lev = [(mk(), mk()) for _ in range(nev)]
+
     def step(i=None):
         if i is not None:
             fev[i][0].record(stream)
-        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+        beta = dn.longhorn_eps(d["k"], d["beta"]) if longhorn else d["beta"]
+        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], beta, d["g"], d["h0"], d["cu_seqlens"])
         if i is not None:
             fev[i][1].record(stream)
         if backward:
-            dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
-                         d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None)
+            # nothing is kept between the passes: the backward recomputes eps
+            beta = dn.longhorn_eps(d["k"], d["beta"]) if longhorn else d["beta"]
+            gr = dn.chunk_bwd(d["q"], d["k"], d["v"], beta, d["g"], d["h0"], d["dO"], d["dhT"],
+                              d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None)
+            if longhorn:
+                if i is not None:
+                    lev[i][0].record(stream)
+                gr["dbeta"] = dn.longhorn_eps_bwd(d["k"], d["beta"], gr["dbeta"], gr["dk"])
+                if i is not None:
+                    lev[i][1].record(stream)
         return o
 
     for _ in range(args.warmup):
@@ -157,6 +172,8 @@ def main():
     if backward:
         for j, name in enumerate(("recompute", "state_grad_scan", "chunk_grad")):
             stage_us[name] = avg([(e[j], e[j + 1]) for e in bev[:args.steps]])
+        if longhorn:
+            stage_us["longhorn_eps_bwd"] = avg(lev[:args.steps])
     flops = fwd_flops(sh) + (bwd_flops(sh) if backward else 0.0)
     if backward:
         kname, kus, kbytes = "dn::bwd_chunk_kernel", stage_us["chunk_grad"], chunk_grad_bytes(sh)
@@ -184,7 +201,7 @@ def main():
         "data": "synthetic (seeded, L2-normalised q/k, sigmoid beta, -softplus*0.1 gate)",
         "config": {"workload": synth.WORKLOAD_NAMES[wid], "B": sh.B, "T": sh.T, "H": sh.H,
                    "Dk": sh.Dk, "Dv": sh.Dv, "chunk": 64, "passes": "fwd+bwd" if backward else "fwd",
-                   "n_seqs": sh.n_seqs},
+                   "n_seqs": sh.n_seqs, "variant": args.variant},
         "roofline": roofline,
         "tflops": round(step_tflops, 2),
         "mfma_frac": round(step_tflops / MFMA_BF16_PEAK_TFS, 4),
@@ -192,13 +209,15 @@ def main():
         "kernel_us": {k: round(v, 2) for k, v in stage_us.items()},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds, args.variant)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(x, sh, backward, budget_s):
+def cpu_baseline(x, sh, backward, budget_s, variant="delta"):
     """The fp64 oracle on a bounded sample: whole sequences of a few heads."""
     import oracle
+    ofwd = oracle.longhorn_fwd if variant == "longhorn" else oracle.fwd
+    obwd = oracle.longhorn_bwd if variant == "longhorn" else oracle.bwd
     cores = len(os.sched_getaffinity(0))
     nthr = int(os.environ.get("OMP_NUM_THREADS", cores) or cores)
     nthr = max(1, min(nthr, cores))
@@ -220,13 +239,13 @@ def cpu_baseline(x, sh, backward, budget_s):
             h0 = h0[:, :1] if h0 is not None else None
             T = L
         t0 = time.perf_counter()
-        oracle.fwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, nthreads=nthr)
+        ofwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, nthreads=nthr)
         if backward:
             dO = sel(x["dO"])
             if sh.lengths is not None:
                 dO = dO[:, :T]
             dhT = torch.stack([x["dhT"][b, h] for b, h in zip(b_idx, h_idx)]).unsqueeze(1)
-            oracle.bwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, dO, dhT, nthreads=nthr)
+            obwd(xs["q"], xs["k"], xs["v"], xs["beta"], xs["g"], h0, dO, dhT, nthreads=nthr)
         elapsed = time.perf_counter() - t0
         if elapsed * 4 > budget_s or npairs >= sh.B * sh.H:
             break

@@ -22,7 +22,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "DeltaRule", "delta_rule",
+__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "longhorn_eps", "longhorn_eps_bwd", "longhorn_fwd",
+           "longhorn_bwd", "DeltaRule", "delta_rule",
            "load_library", "LIB_PATH", "DnError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")
@@ -72,6 +73,10 @@ def load_library():
     lib.dn_chunk_bwd_events.restype = ctypes.c_int
     lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
     lib.dn_recurrent_step.restype = ctypes.c_int
+    lib.dn_longhorn_eps.argtypes = [ctypes.c_int32] * 5 + [P] * 3 + [P]
+    lib.dn_longhorn_eps.restype = ctypes.c_int
+    lib.dn_longhorn_eps_bwd.argtypes = [ctypes.c_int32] * 5 + [P] * 5 + [P]
+    lib.dn_longhorn_eps_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -224,6 +229,64 @@ def recurrent_step(q, k, v, beta, g, state):
         B, H, Dk, Dv, _DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
         _ptr(state), _ptr(o), _stream(dev)))
     return o
+
+
+def _key_rows(k, beta):
+    """(B, T, H, Dk) of a key tensor [B,T,H,Dk] or a decode key [B,H,Dk]."""
+    if k.dim() == 3:
+        B, H, Dk = k.shape
+        T = 1
+    elif k.dim() == 4:
+        B, T, H, Dk = k.shape
+    else:
+        raise ValueError("k must be [B,T,H,Dk] or [B,H,Dk]")
+    if k.dtype not in _DTYPES or k.device.type != "cuda":
+        raise ValueError("k must be a float32/bfloat16 GPU tensor")
+    _need(k, "k", k.dtype, tuple(k.shape), k.device)
+    _need(beta, "beta", torch.float32, tuple(k.shape[:-1]), k.device)
+    return B, T, H, Dk
+
+
+def longhorn_eps(k, beta):
+    """Longhorn step size eps = beta / (1 + beta |k|^2) (``dn_longhorn_eps``),
+    float32 with beta's shape; feed it to ``chunk_fwd`` / ``recurrent_step``
+    as beta to run the Longhorn recurrence."""
+    lib = load_library()
+    B, T, H, Dk = _key_rows(k, beta)
+    eps = torch.empty(beta.shape, dtype=torch.float32, device=k.device)
+    _check("dn_longhorn_eps", lib.dn_longhorn_eps(
+        B, T, H, Dk, _DTYPES[k.dtype], _ptr(k), _ptr(beta), _ptr(eps), _stream(k.device)))
+    return eps
+
+
+def longhorn_eps_bwd(k, beta, deps, dk):
+    """Backward of ``longhorn_eps`` (``dn_longhorn_eps_bwd``): returns dbeta and
+    adds the key term into ``dk`` (float32, updated in place)."""
+    lib = load_library()
+    B, T, H, Dk = _key_rows(k, beta)
+    _need(deps, "deps", torch.float32, tuple(beta.shape), k.device)
+    _need(dk, "dk", torch.float32, tuple(k.shape), k.device)
+    dbeta = torch.empty(beta.shape, dtype=torch.float32, device=k.device)
+    _check("dn_longhorn_eps_bwd", lib.dn_longhorn_eps_bwd(
+        B, T, H, Dk, _DTYPES[k.dtype], _ptr(k), _ptr(beta), _ptr(deps), _ptr(dbeta), _ptr(dk),
+        _stream(k.device)))
+    return dbeta
+
+
+def longhorn_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_state=True):
+    """Forward pass of the Longhorn recurrence: ``longhorn_eps`` then
+    ``chunk_fwd`` at beta := eps.  Returns (o, hT)."""
+    return chunk_fwd(q, k, v, longhorn_eps(k, beta), g, h0, cu_seqlens, output_final_state)
+
+
+def longhorn_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, workspace=None):
+    """Backward pass of the Longhorn recurrence: eps again (nothing is kept
+    from the forward call), ``chunk_bwd`` at beta := eps, then
+    ``longhorn_eps_bwd``.  Returns the gradient dict of ``chunk_bwd``."""
+    eps = longhorn_eps(k, beta)
+    gr = chunk_bwd(q, k, v, eps, g, h0, dO, dhT, cu_seqlens, workspace=workspace)
+    gr["dbeta"] = longhorn_eps_bwd(k, beta, gr["dbeta"], gr["dk"])
+    return gr
 
 
 class DeltaRule(torch.autograd.Function):

@@ -240,4 +240,45 @@ dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_
   return from_hip(dn::launch_step(p, dtype, Dk, stream));
 }
 
+static dn_status longhorn_check(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype) {
+  if (B <= 0 || T < 0 || H <= 0) return DN_EINVAL;
+  if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+  if (Dk != 64 && Dk != 128) return DN_EUNSUPPORTED;
+  if ((int64_t)B * T * H / 4 >= (int64_t)1 << 31) return DN_EUNSUPPORTED;  // grid size
+  return DN_OK;
+}
+
+dn_status dn_longhorn_eps(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype, const void *k,
+                          const float *beta, float *eps, hipStream_t stream) {
+  dn_status st = longhorn_check(B, T, H, Dk, dtype);
+  if (st != DN_OK) return st;
+  const int64_t rows = (int64_t)B * T * H;
+  if (rows == 0) return DN_OK;
+  if (!k || !beta || !eps || !aligned16(k)) return DN_EINVAL;
+  dn::LonghornParams p = {};
+  p.k = k;
+  p.beta = beta;
+  p.eps = eps;
+  p.rows = rows;
+  return from_hip(dn::launch_longhorn(p, dtype, Dk, stream));
+}
+
+dn_status dn_longhorn_eps_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype, const void *k,
+                              const float *beta, const float *deps, float *dbeta, float *dk,
+                              hipStream_t stream) {
+  dn_status st = longhorn_check(B, T, H, Dk, dtype);
+  if (st != DN_OK) return st;
+  const int64_t rows = (int64_t)B * T * H;
+  if (rows == 0) return DN_OK;
+  if (!k || !beta || !deps || !dbeta || !dk || !aligned16(k) || !aligned16(dk)) return DN_EINVAL;
+  dn::LonghornParams p = {};
+  p.k = k;
+  p.beta = beta;
+  p.deps = deps;
+  p.dbeta = dbeta;
+  p.dk = dk;
+  p.rows = rows;
+  return from_hip(dn::launch_longhorn(p, dtype, Dk, stream));
+}
+
 }  // extern "C"

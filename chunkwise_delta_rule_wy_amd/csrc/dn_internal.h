@@ -44,6 +44,16 @@ struct StepParams {
   int B, H, DV;
 };
 
+// Longhorn step size (eps set) or its backward (dk set): rows = B T H key rows
+struct LonghornParams {
+  const void *k;
+  const float *beta;
+  float *eps;                 // forward output
+  const float *deps;          // backward input
+  float *dbeta, *dk;          // backward outputs (dk accumulated)
+  int64_t rows;
+};
+
 struct SeqInfo {
   int b, t0, len;
 };
@@ -83,6 +93,7 @@ hipError_t launch_fwd(const FwdParams &p, int dtype, int DK, bool store_states, 
 hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_states,
                           bool write_o, hipStream_t stream);
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
+hipError_t launch_longhorn(const LonghornParams &p, int dtype, int DK, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);
 // ev_scan / ev_chunk (may be null) are recorded on `stream` after the scan and

@@ -142,6 +142,37 @@ dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_
                             const float *beta, const float *g,
                             float *state, void *o, hipStream_t stream);
 
+/*
+ * Longhorn step size (Gated DeltaNet review thread, Table 1, row "Longhorn",
+ * with the caption's scalar beta): the Longhorn recurrence is the delta rule
+ * with beta_t replaced by
+ *
+ *     eps_t = beta_t / (1 + beta_t k_t^T k_t),
+ *
+ * so it runs as dn_longhorn_eps followed by dn_chunk_fwd / dn_recurrent_step
+ * with beta := eps.  The table's row has no decay; a gate g given to those
+ * calls still multiplies the state.
+ * k [B,T,H,Dk] (dtype, for decode T = 1), beta and eps [B,T,H] fp32; rows are
+ * independent.  Supported: Dk in {64, 128}; k 16-byte aligned.  T == 0 is a
+ * no-op.  Nothing is allocated; the call enqueues one kernel on `stream`.
+ */
+dn_status dn_longhorn_eps(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype,
+                          const void *k, const float *beta, float *eps, hipStream_t stream);
+
+/*
+ * Backward of dn_longhorn_eps (the chain rule through eps; s = k^T k):
+ *
+ *     dbeta = deps / (1 + beta s)^2
+ *     dk   += deps * (-2 beta^2 / (1 + beta s)^2) * k
+ *
+ * deps is the beta-gradient that dn_chunk_bwd returns when it is called with
+ * beta := eps; dk [B,T,H,Dk] fp32 (16-byte aligned) is the key gradient of
+ * that call and is updated in place.  dbeta may alias deps.
+ */
+dn_status dn_longhorn_eps_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype,
+                              const void *k, const float *beta, const float *deps,
+                              float *dbeta, float *dk, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -116,3 +116,20 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 64, 1, 64)
     with pytest.raises(ValueError):
         dn.chunk_fwd(q, q, q, torch.zeros(1, 64, 1))
+
+
+def test_longhorn_validation(lib):
+    P = ctypes.c_void_p
+    f = lib.dn_longhorn_eps
+    assert f(0, 1, 1, 64, 1, P(FAKE), P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert f(1, -1, 1, 64, 1, P(FAKE), P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert f(1, 1, 1, 96, 1, P(FAKE), P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED
+    assert f(1, 1, 1, 64, 7, P(FAKE), P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert f(1, 1, 1, 64, 1, P(FAKE + 4), P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert f(1, 1, 1, 64, 1, P(FAKE), None, P(FAKE), None) == DN_EINVAL
+    assert f(1, 0, 1, 64, 1, None, None, None, None) == DN_OK  # nothing to do, nothing launched
+    fb = lib.dn_longhorn_eps_bwd
+    assert fb(1, 1, 1, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None) == DN_EINVAL
+    assert fb(1, 1, 1, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE + 4), None) == DN_EINVAL
+    assert fb(1, 1, 1, 128, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert fb(2, 3, 1, 32, 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED

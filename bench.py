@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 # FETCH_SIZE and WRITE_SIZE scaled by what the same counters read for a copy of
 # known size (commands and raw counts under profiles/); it describes the kernel as
 # built when the counters were taken
-CHUNK_GRAD_TRAFFIC_W4 = 1511.2e6
+CHUNK_GRAD_TRAFFIC_W4 = 1511.6e6
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
 
 
@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--workload", default="4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy a 512 MiB fp32 tensor once (torch copy_): "
+                         "the kernel of known size that calibrates rocprofv3 byte counters")
     ap.add_argument("--variant", choices=("delta", "longhorn"), default="delta",
                     help="longhorn: the step size eps = beta / (1 + beta |k|^2) of Table 1's "
                          "Longhorn row, computed (and differentiated) around the same passes")
@@ -208,6 +211,17 @@ def main():
         "step_gbs": round(workload_bytes(sh, backward) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 2) for k, v in stage_us.items()},
     }
+    if args.copy_calibration:
+        a = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        e0, e1 = mk(), mk()
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        e1.synchronize()
+        out["copy_512MiB_us"] = round(e0.elapsed_time(e1) * 1e3, 1)
+        del a, b
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds, args.variant)
     print(json.dumps(out), flush=True)

@@ -8,7 +8,9 @@ its Python binding) never touches it, and the two share no code: this wraps
 S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t),
 its sequential adjoint, and a single recurrent step; and the Longhorn row of
 the same table (the delta rule at the step size beta / (1 + beta |k|^2)),
-with its gradient by the chain rule through that step size.
+with its gradient by the chain rule through that step size; and the input
+prologue of the workloads (L2-normalised q and k, sigmoid beta, negative
+softplus log-gate) with its gradient, in numpy float64.
 
 Inputs may be torch tensors (any float dtype, on any device) or numpy arrays;
 they are upcast exactly to float64 on the host.  Results are float64 numpy.
@@ -179,3 +181,43 @@ def longhorn_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, nthreads=0
     gr["dbeta"] = dbeta
     gr["dk"] = gr["dk"] + dk_extra
     return gr
+
+
+# ------------------------------------------------------------- input prologue
+# The steps on either side of the recurrence in a (Gated) DeltaNet layer, as
+# the workloads prepare their inputs: q and k are L2-normalised per token and
+# head, beta = sigmoid(b), and the log-gate is g = -c * softplus(x).  A zero
+# row normalises to zero with a zero gradient (the direction is undefined).
+
+def prologue(q_in, k_in, b_in, g_in=None, gate_scale=1.0):
+    """Returns (q, k, beta, g) in float64 (g None without a gate input)."""
+    q_in, k_in, b_in, g_in = map(_f64, (q_in, k_in, b_in, g_in))
+
+    def unit(x):
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+    beta = 1.0 / (1.0 + np.exp(-b_in))
+    g = None
+    if g_in is not None:
+        g = -float(gate_scale) * (np.maximum(g_in, 0.0) + np.log1p(np.exp(-np.abs(g_in))))
+    return unit(q_in), unit(k_in), beta, g
+
+
+def prologue_bwd(q_in, k_in, b_in, g_in, gate_scale, dq, dk, dbeta, dg=None):
+    """Gradients of the prologue's inputs from those of its outputs:
+    d x_in = (dx - u (u . dx)) / |x| with u = x / |x| (0 for a zero row),
+    d b_in = dbeta * beta (1 - beta), d g_in = -c * sigmoid(x) * dg."""
+    q_in, k_in, b_in, g_in, dq, dk, dbeta, dg = map(_f64, (q_in, k_in, b_in, g_in, dq, dk, dbeta, dg))
+
+    def unit_bwd(x, dx):
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        safe = np.where(n > 0, n, 1.0)
+        u = x / safe
+        r = (dx - u * np.sum(u * dx, axis=-1, keepdims=True)) / safe
+        return np.where(n > 0, r, 0.0)
+    beta = 1.0 / (1.0 + np.exp(-b_in))
+    db_in = dbeta * beta * (1.0 - beta)
+    dg_in = None
+    if g_in is not None:
+        dg_in = -float(gate_scale) * dg / (1.0 + np.exp(-g_in))
+    return unit_bwd(q_in, dq), unit_bwd(k_in, dk), db_in, dg_in

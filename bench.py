@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy a 512 MiB fp32 tensor once (torch copy_): "
                          "the kernel of known size that calibrates rocprofv3 byte counters")
+    ap.add_argument("--prologue", action="store_true",
+                    help="start from the raw draws: the input prologue (L2-normalised q, k; "
+                         "sigmoid beta; -0.1 softplus gate) and its backward run around the passes")
     ap.add_argument("--variant", choices=("delta", "longhorn"), default="delta",
                     help="longhorn: the step size eps = beta / (1 + beta |k|^2) of Table 1's "
                          "Longhorn row, computed (and differentiated) around the same passes")
@@ -117,7 +120,7 @@ def main():
     wid = int(wid)
     sh = synth.WORKLOADS[wid]
     backward = sh.backward
-    x = synth.workload_inputs(wid)
+    x = synth.workload_inputs(wid, raw=args.prologue)
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
     torch.cuda.synchronize()
 
@@ -137,24 +140,42 @@ def main():
     longhorn = args.variant == "longhorn"
     lev = [(mk(), mk()) for _ in range(nev)]
 
+    pev = [(mk(), mk()) for _ in range(nev)]
+    pbev = [(mk(), mk()) for _ in range(nev)]
+
     def step(i=None):
+        if args.prologue:
+            if i is not None:
+                pev[i][0].record(stream)
+            q, k, b0, g = dn.prologue(d["q_in"], d["k_in"], d["b_in"], d["x_in"], d["gate_scale"])
+            if i is not None:
+                pev[i][1].record(stream)
+        else:
+            q, k, b0, g = d["q"], d["k"], d["beta"], d["g"]
         if i is not None:
             fev[i][0].record(stream)
-        beta = dn.longhorn_eps(d["k"], d["beta"]) if longhorn else d["beta"]
-        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], beta, d["g"], d["h0"], d["cu_seqlens"])
+        beta = dn.longhorn_eps(k, b0) if longhorn else b0
+        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], d["cu_seqlens"])
         if i is not None:
             fev[i][1].record(stream)
         if backward:
             # nothing is kept between the passes: the backward recomputes eps
-            beta = dn.longhorn_eps(d["k"], d["beta"]) if longhorn else d["beta"]
-            gr = dn.chunk_bwd(d["q"], d["k"], d["v"], beta, d["g"], d["h0"], d["dO"], d["dhT"],
+            beta = dn.longhorn_eps(k, b0) if longhorn else b0
+            gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"],
                               d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None)
             if longhorn:
                 if i is not None:
                     lev[i][0].record(stream)
-                gr["dbeta"] = dn.longhorn_eps_bwd(d["k"], d["beta"], gr["dbeta"], gr["dk"])
+                gr["dbeta"] = dn.longhorn_eps_bwd(k, b0, gr["dbeta"], gr["dk"])
                 if i is not None:
                     lev[i][1].record(stream)
+            if args.prologue:
+                if i is not None:
+                    pbev[i][0].record(stream)
+                dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], d["gate_scale"],
+                                gr["dq"], gr["dk"], gr["dbeta"], gr["dg"])
+                if i is not None:
+                    pbev[i][1].record(stream)
         return o
 
     for _ in range(args.warmup):
@@ -177,6 +198,10 @@ def main():
             stage_us[name] = avg([(e[j], e[j + 1]) for e in bev[:args.steps]])
         if longhorn:
             stage_us["longhorn_eps_bwd"] = avg(lev[:args.steps])
+        if args.prologue:
+            stage_us["prologue_bwd"] = avg(pbev[:args.steps])
+    if args.prologue:
+        stage_us["prologue"] = avg(pev[:args.steps])
     flops = fwd_flops(sh) + (bwd_flops(sh) if backward else 0.0)
     if backward:
         kname, kus, kbytes = "dn::bwd_chunk_kernel", stage_us["chunk_grad"], chunk_grad_bytes(sh)
@@ -204,7 +229,7 @@ def main():
         "data": "synthetic (seeded, L2-normalised q/k, sigmoid beta, -softplus*0.1 gate)",
         "config": {"workload": synth.WORKLOAD_NAMES[wid], "B": sh.B, "T": sh.T, "H": sh.H,
                    "Dk": sh.Dk, "Dv": sh.Dv, "chunk": 64, "passes": "fwd+bwd" if backward else "fwd",
-                   "n_seqs": sh.n_seqs, "variant": args.variant},
+                   "n_seqs": sh.n_seqs, "variant": args.variant, "prologue": args.prologue},
         "roofline": roofline,
         "tflops": round(step_tflops, 2),
         "mfma_frac": round(step_tflops / MFMA_BF16_PEAK_TFS, 4),

@@ -23,7 +23,7 @@ from typing import Optional
 import torch
 
 __all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "longhorn_eps", "longhorn_eps_bwd", "longhorn_fwd",
-           "longhorn_bwd", "DeltaRule", "delta_rule",
+           "longhorn_bwd", "prologue", "prologue_bwd", "DeltaRule", "delta_rule",
            "load_library", "LIB_PATH", "DnError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")
@@ -77,6 +77,10 @@ def load_library():
     lib.dn_longhorn_eps.restype = ctypes.c_int
     lib.dn_longhorn_eps_bwd.argtypes = [ctypes.c_int32] * 5 + [P] * 5 + [P]
     lib.dn_longhorn_eps_bwd.restype = ctypes.c_int
+    lib.dn_prologue.argtypes = [ctypes.c_int32] * 5 + [P] * 4 + [ctypes.c_float] + [P] * 4 + [P]
+    lib.dn_prologue.restype = ctypes.c_int
+    lib.dn_prologue_bwd.argtypes = [ctypes.c_int32] * 5 + [P] * 4 + [ctypes.c_float] + [P] * 8 + [P]
+    lib.dn_prologue_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -287,6 +291,48 @@ def longhorn_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, workspace=
     gr = chunk_bwd(q, k, v, eps, g, h0, dO, dhT, cu_seqlens, workspace=workspace)
     gr["dbeta"] = longhorn_eps_bwd(k, beta, gr["dbeta"], gr["dk"])
     return gr
+
+
+def prologue(q_in, k_in, b_in, x_in=None, gate_scale: float = 1.0):
+    """Input prologue (``dn_prologue``): q, k L2-normalised per row (dtype of
+    q_in), beta = sigmoid(b_in), g = -gate_scale * softplus(x_in) (None
+    without x_in).  Returns (q, k, beta, g)."""
+    lib = load_library()
+    B, T, H, Dk = _key_rows(k_in, b_in)
+    _need(q_in, "q_in", k_in.dtype, tuple(k_in.shape), k_in.device)
+    _need(x_in, "x_in", torch.float32, tuple(b_in.shape), k_in.device)
+    q = torch.empty_like(q_in)
+    k = torch.empty_like(k_in)
+    beta = torch.empty_like(b_in)
+    g = torch.empty_like(x_in) if x_in is not None else None
+    _check("dn_prologue", lib.dn_prologue(
+        B, T, H, Dk, _DTYPES[k_in.dtype], _ptr(q_in), _ptr(k_in), _ptr(b_in), _ptr(x_in),
+        float(gate_scale), _ptr(q), _ptr(k), _ptr(beta), _ptr(g), _stream(k_in.device)))
+    return q, k, beta, g
+
+
+def prologue_bwd(q_in, k_in, b_in, x_in, gate_scale, dq, dk, dbeta, dg=None):
+    """Backward of ``prologue`` (``dn_prologue_bwd``): float32 gradients
+    (dq_in, dk_in, db_in, dx_in) from those of q, k, beta, g."""
+    lib = load_library()
+    B, T, H, Dk = _key_rows(k_in, b_in)
+    dev = k_in.device
+    _need(q_in, "q_in", k_in.dtype, tuple(k_in.shape), dev)
+    _need(x_in, "x_in", torch.float32, tuple(b_in.shape), dev)
+    _need(dq, "dq", torch.float32, tuple(k_in.shape), dev)
+    _need(dk, "dk", torch.float32, tuple(k_in.shape), dev)
+    _need(dbeta, "dbeta", torch.float32, tuple(b_in.shape), dev)
+    _need(dg, "dg", torch.float32, tuple(b_in.shape), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq_in = torch.empty(k_in.shape, **f32)
+    dk_in = torch.empty(k_in.shape, **f32)
+    db_in = torch.empty(b_in.shape, **f32)
+    dx_in = torch.empty(b_in.shape, **f32) if x_in is not None else None
+    _check("dn_prologue_bwd", lib.dn_prologue_bwd(
+        B, T, H, Dk, _DTYPES[k_in.dtype], _ptr(q_in), _ptr(k_in), _ptr(b_in), _ptr(x_in),
+        float(gate_scale), _ptr(dq), _ptr(dk), _ptr(dbeta), _ptr(dg), _ptr(dq_in), _ptr(dk_in),
+        _ptr(db_in), _ptr(dx_in), _stream(dev)))
+    return dq_in, dk_in, db_in, dx_in
 
 
 class DeltaRule(torch.autograd.Function):

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdn.so")
-SOURCES = ["dn_api.hip", "dn_fwd.hip", "dn_fwd_f32.hip", "dn_bwd.hip", "dn_scan.hip", "dn_bwd_chunk.hip", "dn_step.hip", "dn_longhorn.hip"]
+SOURCES = ["dn_api.hip", "dn_fwd.hip", "dn_fwd_f32.hip", "dn_bwd.hip", "dn_scan.hip", "dn_bwd_chunk.hip", "dn_step.hip", "dn_longhorn.hip", "dn_prologue.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -240,7 +240,7 @@ dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_
   return from_hip(dn::launch_step(p, dtype, Dk, stream));
 }
 
-static dn_status longhorn_check(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype) {
+static dn_status rows_check(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype) {
   if (B <= 0 || T < 0 || H <= 0) return DN_EINVAL;
   if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
   if (Dk != 64 && Dk != 128) return DN_EUNSUPPORTED;
@@ -250,7 +250,7 @@ static dn_status longhorn_check(int32_t B, int32_t T, int32_t H, int32_t Dk, int
 
 dn_status dn_longhorn_eps(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype, const void *k,
                           const float *beta, float *eps, hipStream_t stream) {
-  dn_status st = longhorn_check(B, T, H, Dk, dtype);
+  dn_status st = rows_check(B, T, H, Dk, dtype);
   if (st != DN_OK) return st;
   const int64_t rows = (int64_t)B * T * H;
   if (rows == 0) return DN_OK;
@@ -266,7 +266,7 @@ dn_status dn_longhorn_eps(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t d
 dn_status dn_longhorn_eps_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype, const void *k,
                               const float *beta, const float *deps, float *dbeta, float *dk,
                               hipStream_t stream) {
-  dn_status st = longhorn_check(B, T, H, Dk, dtype);
+  dn_status st = rows_check(B, T, H, Dk, dtype);
   if (st != DN_OK) return st;
   const int64_t rows = (int64_t)B * T * H;
   if (rows == 0) return DN_OK;
@@ -279,6 +279,61 @@ dn_status dn_longhorn_eps_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32
   p.dk = dk;
   p.rows = rows;
   return from_hip(dn::launch_longhorn(p, dtype, Dk, stream));
+}
+
+dn_status dn_prologue(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype, const void *q_in,
+                      const void *k_in, const float *b_in, const float *x_in, float gate_scale, void *q,
+                      void *k, float *beta, float *g, hipStream_t stream) {
+  dn_status st = rows_check(B, T, H, Dk, dtype);
+  if (st != DN_OK) return st;
+  if ((x_in == nullptr) != (g == nullptr)) return DN_EINVAL;
+  const int64_t rows = (int64_t)B * T * H;
+  if (rows == 0) return DN_OK;
+  if (!q_in || !k_in || !b_in || !q || !k || !beta) return DN_EINVAL;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q) || !aligned16(k)) return DN_EINVAL;
+  dn::PrologueParams p = {};
+  p.q_in = q_in;
+  p.k_in = k_in;
+  p.b_in = b_in;
+  p.x_in = x_in;
+  p.gate_scale = gate_scale;
+  p.q = q;
+  p.k = k;
+  p.beta = beta;
+  p.g = g;
+  p.rows = rows;
+  return from_hip(dn::launch_prologue(p, dtype, Dk, false, stream));
+}
+
+dn_status dn_prologue_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype, const void *q_in,
+                          const void *k_in, const float *b_in, const float *x_in, float gate_scale,
+                          const float *dq, const float *dk, const float *dbeta, const float *dg,
+                          float *dq_in, float *dk_in, float *db_in, float *dx_in, hipStream_t stream) {
+  dn_status st = rows_check(B, T, H, Dk, dtype);
+  if (st != DN_OK) return st;
+  if ((x_in == nullptr) != (dg == nullptr) || (x_in == nullptr) != (dx_in == nullptr)) return DN_EINVAL;
+  const int64_t rows = (int64_t)B * T * H;
+  if (rows == 0) return DN_OK;
+  if (!q_in || !k_in || !b_in || !dq || !dk || !dbeta || !dq_in || !dk_in || !db_in) return DN_EINVAL;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(dq) || !aligned16(dk) || !aligned16(dq_in) ||
+      !aligned16(dk_in))
+    return DN_EINVAL;
+  dn::PrologueParams p = {};
+  p.q_in = q_in;
+  p.k_in = k_in;
+  p.b_in = b_in;
+  p.x_in = x_in;
+  p.gate_scale = gate_scale;
+  p.dq = dq;
+  p.dk = dk;
+  p.dbeta = dbeta;
+  p.dg = dg;
+  p.dq_in = dq_in;
+  p.dk_in = dk_in;
+  p.db_in = db_in;
+  p.dx_in = dx_in;
+  p.rows = rows;
+  return from_hip(dn::launch_prologue(p, dtype, Dk, true, stream));
 }
 
 }  // extern "C"

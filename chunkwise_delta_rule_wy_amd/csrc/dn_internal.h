@@ -54,6 +54,19 @@ struct LonghornParams {
   int64_t rows;
 };
 
+// Input prologue (forward: q, k, beta, g from q_in, k_in, b_in, x_in) and its
+// backward (dq_in, dk_in, db_in, dx_in from dq, dk, dbeta, dg); rows = B T H
+struct PrologueParams {
+  const void *q_in, *k_in;
+  const float *b_in, *x_in;   // x_in null: no gate
+  float gate_scale;
+  void *q, *k;
+  float *beta, *g;
+  const float *dq, *dk, *dbeta, *dg;
+  float *dq_in, *dk_in, *db_in, *dx_in;
+  int64_t rows;
+};
+
 struct SeqInfo {
   int b, t0, len;
 };
@@ -94,6 +107,7 @@ hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_stat
                           bool write_o, hipStream_t stream);
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
 hipError_t launch_longhorn(const LonghornParams &p, int dtype, int DK, hipStream_t stream);
+hipError_t launch_prologue(const PrologueParams &p, int dtype, int DK, bool backward, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);
 // ev_scan / ev_chunk (may be null) are recorded on `stream` after the scan and

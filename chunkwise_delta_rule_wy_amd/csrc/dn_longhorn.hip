@@ -11,34 +11,13 @@
 // kernels read each key row once, 16 bytes per lane (Dk / 8 lanes for bf16,
 // Dk / 4 for fp32), and are bound by HBM bandwidth; the squared norm is a sum
 // over the row's lanes, which sit in one wave.
-#include "dn_internal.h"
+#include "dn_rows.h"
 
 namespace dn {
 namespace {
 
-constexpr int LH_THREADS = 256;
-
-template <typename E> struct Vec16;  // 16 bytes of a key row
-template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int N = 8; };
-template <> struct Vec16<float> { typedef f32x4 type; static constexpr int N = 4; };
-
-template <int LANES>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < LANES; m <<= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
-
 template <typename E, int DK>
-struct RowMap {
-  static constexpr int PER = Vec16<E>::N;       // key elements per lane
-  static constexpr int LANES = DK / PER;        // lanes per row (8 .. 32)
-  static constexpr int RPB = LH_THREADS / LANES;  // rows per workgroup
-  static_assert(LANES <= 64 && 64 % LANES == 0, "a row sits in one wave");
-};
-
-template <typename E, int DK>
-__global__ __launch_bounds__(LH_THREADS) void eps_kernel(const E *__restrict__ k, const float *__restrict__ beta,
+__global__ __launch_bounds__(ROW_THREADS) void eps_kernel(const E *__restrict__ k, const float *__restrict__ beta,
                                                          float *__restrict__ eps, int64_t rows) {
   using RM = RowMap<E, DK>;
   const int64_t row = (int64_t)blockIdx.x * RM::RPB + threadIdx.x / RM::LANES;
@@ -61,7 +40,7 @@ __global__ __launch_bounds__(LH_THREADS) void eps_kernel(const E *__restrict__ k
 }
 
 template <typename E, int DK>
-__global__ __launch_bounds__(LH_THREADS) void eps_bwd_kernel(const E *__restrict__ k, const float *__restrict__ beta,
+__global__ __launch_bounds__(ROW_THREADS) void eps_bwd_kernel(const E *__restrict__ k, const float *__restrict__ beta,
                                                              const float *deps, float *dbeta, float *__restrict__ dk,
                                                              int64_t rows) {
   using RM = RowMap<E, DK>;
@@ -104,10 +83,10 @@ hipError_t launch_t(const LonghornParams &p, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   const E *k = static_cast<const E *>(p.k);
   if (p.dk)
-    hipLaunchKernelGGL((eps_bwd_kernel<E, DK>), dim3((unsigned)blocks), dim3(LH_THREADS), 0, stream, k, p.beta,
+    hipLaunchKernelGGL((eps_bwd_kernel<E, DK>), dim3((unsigned)blocks), dim3(ROW_THREADS), 0, stream, k, p.beta,
                        p.deps, p.dbeta, p.dk, p.rows);
   else
-    hipLaunchKernelGGL((eps_kernel<E, DK>), dim3((unsigned)blocks), dim3(LH_THREADS), 0, stream, k, p.beta, p.eps,
+    hipLaunchKernelGGL((eps_kernel<E, DK>), dim3((unsigned)blocks), dim3(ROW_THREADS), 0, stream, k, p.beta, p.eps,
                        p.rows);
   return hipGetLastError();
 }

@@ -98,28 +98,37 @@ def _unit_rows(x: torch.Tensor) -> torch.Tensor:
     return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
 
 
-def make_inputs(shape: Shape, seed: int, *, beta_override: Optional[float] = None) -> dict:
+GATE_SCALE = 0.1  # g = -GATE_SCALE * softplus(noise)
+
+
+def make_inputs(shape: Shape, seed: int, *, beta_override: Optional[float] = None,
+                raw: bool = False) -> dict:
     """Draw one seeded input set on the CPU.
 
     Returns a dict with q, k, v (``shape.dtype``), beta, g (fp32 or None),
     h0 (fp32 or None), cu_seqlens (int32 or None) and, for backward settings,
-    dO (``shape.dtype``) and dhT (fp32).  Tensors are contiguous, in the
+    dO (``shape.dtype``) and dhT (fp32).  With ``raw`` it also holds the draws
+    before preparation: q_in, k_in (``shape.dtype``), b_in (beta logits) and
+    x_in (gate noise, None when ungated), with ``gate_scale``.  Tensors are contiguous, in the
     layouts q,k ``[B,T,H,Dk]``, v ``[B,T,H,Dv]``, beta/g ``[B,T,H]``,
     h0 ``[N,H,Dk,Dv]`` (the transposed state).
     """
     gen = torch.Generator("cpu").manual_seed(seed)
     B, T, H, Dk, Dv = shape.B, shape.T, shape.H, shape.Dk, shape.Dv
     N = shape.n_seqs
-    q = _unit_rows(torch.randn(B, T, H, Dk, generator=gen))
-    k = _unit_rows(torch.randn(B, T, H, Dk, generator=gen))
+    q_raw = torch.randn(B, T, H, Dk, generator=gen)
+    k_raw = torch.randn(B, T, H, Dk, generator=gen)
+    q = _unit_rows(q_raw)
+    k = _unit_rows(k_raw)
     v = torch.randn(B, T, H, Dv, generator=gen)
-    beta = torch.sigmoid(torch.randn(B, T, H, generator=gen))
+    b_raw = torch.randn(B, T, H, generator=gen)
+    beta = torch.sigmoid(b_raw)
     if beta_override is not None:
         beta = torch.full_like(beta, float(beta_override))
     g = None
     noise = torch.randn(B, T, H, generator=gen)
     if shape.gated:
-        g = -torch.nn.functional.softplus(noise) * 0.1
+        g = -torch.nn.functional.softplus(noise) * GATE_SCALE
     h0 = None
     h0_draw = torch.randn(N, H, Dk, Dv, generator=gen) * 0.1
     if shape.has_h0:
@@ -136,12 +145,18 @@ def make_inputs(shape: Shape, seed: int, *, beta_override: Optional[float] = Non
     if shape.backward:
         out["dO"] = torch.randn(B, T, H, Dv, generator=gen).to(shape.dtype).contiguous()
         out["dhT"] = (torch.randn(N, H, Dk, Dv, generator=gen) * 0.1).contiguous()
+    if raw:
+        out["q_in"] = q_raw.to(shape.dtype).contiguous()
+        out["k_in"] = k_raw.to(shape.dtype).contiguous()
+        out["b_in"] = b_raw.contiguous()
+        out["x_in"] = noise.contiguous() if shape.gated else None
+        out["gate_scale"] = GATE_SCALE
     return out
 
 
-def workload_inputs(wid: int) -> dict:
+def workload_inputs(wid: int, raw: bool = False) -> dict:
     """Inputs of a numbered workload, seeded with ``1000 + wid``."""
-    return make_inputs(WORKLOADS[wid], 1000 + wid)
+    return make_inputs(WORKLOADS[wid], 1000 + wid, raw=raw)
 
 
 def decode_inputs(B: int = 256, H: int = 32, Dk: int = 128, Dv: int = 128,

@@ -173,6 +173,43 @@ dn_status dn_longhorn_eps_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32
                               const void *k, const float *beta, const float *deps,
                               float *dbeta, float *dk, hipStream_t stream);
 
+/*
+ * Input prologue of a (Gated) DeltaNet layer: the preparation applied to the
+ * projections before the recurrence, one fused pass per (token, head) row.
+ * The pages name the layer's parts around the token mixer (the DeltaNet
+ * rebuttal, answer W2: depthwise short convolutions; Table 1: beta, alpha)
+ * but give no formula; this is the preparation the workloads use:
+ *
+ *     q = q_in / |q_in|,  k = k_in / |k_in|     (a zero row stays zero)
+ *     beta = sigmoid(b_in),  g = -gate_scale * softplus(x_in)
+ *
+ * q_in, k_in, q, k [B,T,H,Dk] (dtype, 16-byte aligned); b_in, x_in, beta, g
+ * [B,T,H] fp32.  x_in == NULL (then g must be NULL too) means no gate.
+ * Supported: Dk in {64, 128}.  T == 0 is a no-op.  The short convolution is
+ * not part of this call.
+ */
+dn_status dn_prologue(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype,
+                      const void *q_in, const void *k_in, const float *b_in, const float *x_in,
+                      float gate_scale, void *q, void *k, float *beta, float *g,
+                      hipStream_t stream);
+
+/*
+ * Backward of dn_prologue: from the gradients w.r.t. its outputs (dq, dk
+ * [B,T,H,Dk] fp32 as dn_chunk_bwd returns them; dbeta, dg [B,T,H] fp32) to
+ * those of its inputs, all fp32:
+ *
+ *     dq_in = (dq - q (q . dq)) / |q_in|   (likewise dk_in; 0 for a zero row)
+ *     db_in = dbeta * beta * (1 - beta),   dx_in = -gate_scale * sigmoid(x_in) * dg
+ *
+ * x_in, dg and dx_in are all NULL or all given.  Outputs may not alias inputs.
+ */
+dn_status dn_prologue_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t dtype,
+                          const void *q_in, const void *k_in, const float *b_in,
+                          const float *x_in, float gate_scale,
+                          const float *dq, const float *dk, const float *dbeta, const float *dg,
+                          float *dq_in, float *dk_in, float *db_in, float *dx_in,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -133,3 +133,20 @@ def test_longhorn_validation(lib):
     assert fb(1, 1, 1, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE + 4), None) == DN_EINVAL
     assert fb(1, 1, 1, 128, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None) == DN_EINVAL
     assert fb(2, 3, 1, 32, 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED
+
+
+def test_prologue_validation(lib):
+    P = ctypes.c_void_p
+    f = lib.dn_prologue
+    ok = [P(FAKE)] * 4
+    assert f(1, 1, 1, 96, 1, *ok, 1.0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED
+    assert f(1, 1, 1, 64, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1.0, P(FAKE), P(FAKE), P(FAKE), None, None) == DN_EINVAL
+    assert f(1, 1, 1, 64, 1, P(FAKE + 8), P(FAKE), P(FAKE), None, 1.0, P(FAKE), P(FAKE), P(FAKE), None, None) == DN_EINVAL
+    assert f(1, 1, 1, 64, 1, P(FAKE), P(FAKE), None, None, 1.0, P(FAKE), P(FAKE), P(FAKE), None, None) == DN_EINVAL
+    assert f(1, 0, 1, 64, 1, None, None, None, None, 1.0, None, None, None, None, None) == DN_OK
+    fb = lib.dn_prologue_bwd
+    args = [P(FAKE)] * 3 + [None, 1.0] + [P(FAKE)] * 3 + [None] + [P(FAKE)] * 3 + [None, None]
+    assert fb(1, 1, 1, 64, 1, *args[:-6], P(FAKE), *args[-5:]) == DN_EINVAL  # dg without x_in
+    bad = list(args)
+    bad[9] = P(FAKE + 4)  # misaligned dq_in
+    assert fb(1, 1, 1, 64, 0, *bad) == DN_EINVAL

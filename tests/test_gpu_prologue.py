@@ -1,0 +1,111 @@
+"""GPU parity of the input prologue (L2-normalised q, k; beta = sigmoid;
+g = -c softplus) and its backward against the fp64 oracle, through the C ABI.
+
+Both are plain fp32 arithmetic on exactly upcast inputs: fp32 outputs within
+1e-5 relative of the oracle, bf16 outputs (q, k) within one bf16 rounding
+(2^-8 relative).  The composed path (prologue, chunkwise forward and
+backward, prologue backward) is checked at the benchmark's shape on sampled
+(batch, head) pairs within relative L2 2e-2, like the recurrence alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunkwise_delta_rule_wy_amd as dn
+from chunkwise_delta_rule_wy_amd import synth
+from chunkwise_delta_rule_wy_amd.synth import Shape, make_inputs, rel_l2
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-2
+
+
+def to_dev(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def max_rel(x, y, floor=1e-30):
+    x = x.detach().double().cpu().numpy()
+    y = np.asarray(y, dtype=np.float64)
+    return float(np.max(np.abs(x - y) / np.maximum(np.abs(y), floor)))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("Dk", [64, 128])
+@pytest.mark.parametrize("gated", [True, False])
+def test_prologue_parity(oracle_lib, dtype, Dk, gated):
+    sh = Shape(2, 91, 3, Dk, 64, dtype, gated, False)
+    x = make_inputs(sh, seed=80 + Dk, raw=True)
+    gen = torch.Generator("cpu").manual_seed(81)
+    # rows of varied norm, and two zero rows
+    x["q_in"] = (x["q_in"].float() * torch.rand(2, 91, 3, 1, generator=gen) * 4).to(dtype).contiguous()
+    x["q_in"][0, 5, 1] = 0
+    x["k_in"][1, 90, 2] = 0
+    x["b_in"] = (x["b_in"] * 4).contiguous()
+    d = to_dev(x)
+    c = x["gate_scale"]
+    q, k, beta, g = dn.prologue(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c)
+    torch.cuda.synchronize()
+    rq, rk, rb, rg = oracle_lib.prologue(x["q_in"], x["k_in"], x["b_in"], x["x_in"], c)
+    tol = 4e-3 if dtype == torch.bfloat16 else 1e-5  # one bf16 rounding is at most 2^-8 relative
+    nz = np.abs(rq) > 0
+    assert max_rel(q.cpu()[torch.from_numpy(nz)], rq[nz]) < tol
+    assert torch.all(q.cpu()[torch.from_numpy(~nz)] == 0)
+    nz = np.abs(rk) > 0
+    assert max_rel(k.cpu()[torch.from_numpy(nz)], rk[nz]) < tol
+    assert max_rel(beta, rb) < 1e-5
+    if gated:
+        assert max_rel(g, rg) < 1e-5
+    else:
+        assert g is None
+
+    dq = torch.randn(x["q_in"].shape, generator=gen)
+    dk = torch.randn(x["k_in"].shape, generator=gen)
+    db = torch.randn(x["b_in"].shape, generator=gen)
+    dg = torch.randn(x["b_in"].shape, generator=gen) if gated else None
+    out = dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c, dq.to(DEV), dk.to(DEV),
+                          db.to(DEV), None if dg is None else dg.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle_lib.prologue_bwd(x["q_in"], x["k_in"], x["b_in"], x["x_in"], c, dq, dk, db, dg)
+    for name, mine, r in zip(("dq_in", "dk_in", "db_in", "dx_in"), out, ref):
+        if r is None:
+            assert mine is None
+            continue
+        assert rel_l2(mine.cpu(), r) < 1e-5, name
+    assert torch.all(out[0].cpu()[0, 5, 1] == 0) and torch.all(out[1].cpu()[1, 90, 2] == 0)
+
+
+def test_prologue_composed_full_size_sampled(oracle_lib):
+    """The benchmark's step with the prologue (B=4 T=4096 H=16 dk=128 dv=256):
+    prologue, forward, backward and prologue backward on the GPU against the
+    oracle's composition, on two (batch, head) pairs."""
+    sh = synth.WORKLOADS[4]
+    x = synth.workload_inputs(4, raw=True)
+    d = to_dev(x)
+    c = x["gate_scale"]
+    q, k, beta, g = dn.prologue(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c)
+    o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"])
+    gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"])
+    din = dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c, gr["dq"], gr["dk"],
+                          gr["dbeta"], gr["dg"])
+    torch.cuda.synchronize()
+    o = o.cpu()
+    din = [t.cpu() for t in din]
+    dv, dh0 = gr["dv"].cpu(), gr["dh0"].cpu()
+    rng = np.random.default_rng(8)
+    for idx in rng.choice(sh.B * sh.H, size=2, replace=False):
+        b, h = int(idx) // sh.H, int(idx) % sh.H
+        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
+        st = lambda t: t[b:b + 1, h:h + 1].contiguous()
+        rq, rk, rb, rg = oracle_lib.prologue(sl(x["q_in"]), sl(x["k_in"]), sl(x["b_in"]), sl(x["x_in"]), c)
+        ro, _ = oracle_lib.fwd(rq, rk, sl(x["v"]), rb, rg, st(x["h0"]))
+        rgr = oracle_lib.bwd(rq, rk, sl(x["v"]), rb, rg, st(x["h0"]), sl(x["dO"]), st(x["dhT"]))
+        rin = oracle_lib.prologue_bwd(sl(x["q_in"]), sl(x["k_in"]), sl(x["b_in"]), sl(x["x_in"]), c,
+                                      rgr["dq"], rgr["dk"], rgr["dbeta"], rgr["dg"])
+        errs = {"o": rel_l2(sl(o), ro), "dv": rel_l2(sl(dv), rgr["dv"]), "dh0": rel_l2(st(dh0), rgr["dh0"])}
+        for name, mine, r in zip(("dq_in", "dk_in", "db_in", "dx_in"), din, rin):
+            errs[name] = rel_l2(sl(mine), r)
+        print("prologue workload 4 pair (%d,%d)" % (b, h), " ".join("%s %.2e" % kv for kv in errs.items()),
+              flush=True)
+        for name, e in errs.items():
+            assert e <= TOL, (name, e)

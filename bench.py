@@ -99,6 +99,10 @@ def main():
     ap.add_argument("--prologue", action="store_true",
                     help="start from the raw draws: the input prologue (L2-normalised q, k; "
                          "sigmoid beta; -0.1 softplus gate) and its backward run around the passes")
+    ap.add_argument("--bwd-mode", choices=("saved", "recompute"), default="saved",
+                    help="saved: the forward pass stores the bf16 chunk states and the backward "
+                         "pass reads them (dn_chunk_fwd_save + dn_chunk_bwd_saved); recompute: "
+                         "the backward pass recomputes them (dn_chunk_bwd)")
     ap.add_argument("--variant", choices=("delta", "longhorn"), default="delta",
                     help="longhorn: the step size eps = beta / (1 + beta |k|^2) of Table 1's "
                          "Longhorn row, computed (and differentiated) around the same passes")
@@ -138,6 +142,7 @@ def main():
     bev = [[mk() for _ in range(4)] for _ in range(nev)] if backward else None
 
     longhorn = args.variant == "longhorn"
+    saved = backward and args.bwd_mode == "saved"
     lev = [(mk(), mk()) for _ in range(nev)]
 
     pev = [(mk(), mk()) for _ in range(nev)]
@@ -155,14 +160,16 @@ def main():
         if i is not None:
             fev[i][0].record(stream)
         beta = dn.longhorn_eps(k, b0) if longhorn else b0
-        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], d["cu_seqlens"])
+        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], d["cu_seqlens"],
+                             save_workspace=ws if saved else None)
         if i is not None:
             fev[i][1].record(stream)
         if backward:
             # nothing is kept between the passes: the backward recomputes eps
             beta = dn.longhorn_eps(k, b0) if longhorn else b0
             gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"],
-                              d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None)
+                              d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None,
+                              saved=saved)
             if longhorn:
                 if i is not None:
                     lev[i][0].record(stream)
@@ -195,6 +202,8 @@ def main():
     stage_us = {"fwd": avg(fev[:args.steps])}
     if backward:
         for j, name in enumerate(("recompute", "state_grad_scan", "chunk_grad")):
+            if j == 0 and saved:
+                continue  # the forward pass stored the states
             stage_us[name] = avg([(e[j], e[j + 1]) for e in bev[:args.steps]])
         if longhorn:
             stage_us["longhorn_eps_bwd"] = avg(lev[:args.steps])
@@ -229,7 +238,8 @@ def main():
         "data": "synthetic (seeded, L2-normalised q/k, sigmoid beta, -softplus*0.1 gate)",
         "config": {"workload": synth.WORKLOAD_NAMES[wid], "B": sh.B, "T": sh.T, "H": sh.H,
                    "Dk": sh.Dk, "Dv": sh.Dv, "chunk": 64, "passes": "fwd+bwd" if backward else "fwd",
-                   "n_seqs": sh.n_seqs, "variant": args.variant, "prologue": args.prologue},
+                   "n_seqs": sh.n_seqs, "variant": args.variant, "prologue": args.prologue,
+                   "bwd_mode": args.bwd_mode if backward else None},
         "roofline": roofline,
         "tflops": round(step_tflops, 2),
         "mfma_frac": round(step_tflops / MFMA_BF16_PEAK_TFS, 4),

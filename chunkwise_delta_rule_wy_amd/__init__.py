@@ -71,6 +71,10 @@ def load_library():
     lib.dn_chunk_bwd.restype = ctypes.c_int
     lib.dn_chunk_bwd_events.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
     lib.dn_chunk_bwd_events.restype = ctypes.c_int
+    lib.dn_chunk_fwd_save.argtypes = [S] + [P] * 9 + [P, ctypes.c_size_t, P]
+    lib.dn_chunk_fwd_save.restype = ctypes.c_int
+    lib.dn_chunk_bwd_saved.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
+    lib.dn_chunk_bwd_saved.restype = ctypes.c_int
     lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
     lib.dn_recurrent_step.restype = ctypes.c_int
     lib.dn_longhorn_eps.argtypes = [ctypes.c_int32] * 5 + [P] * 3 + [P]
@@ -129,13 +133,16 @@ def _shape(q, v, cu_seqlens, chunk):
 
 
 def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_state=True,
-              chunk: int = 64):
+              chunk: int = 64, save_workspace: Optional[torch.Tensor] = None):
     """Chunkwise forward pass.
 
     q, k ``[B,T,H,Dk]``, v ``[B,T,H,Dv]`` (float32 or bfloat16, one dtype);
     beta, g ``[B,T,H]`` float32 (g None: no gate); h0 ``[N,H,Dk,Dv]`` float32
     or None; cu_seqlens int32 ``[N+1]`` on the device for packed sequences
     (then B == 1).  Returns ``(o, hT)`` (hT None unless output_final_state).
+    ``save_workspace`` (uint8, at least ``bwd_workspace_bytes``; bfloat16
+    inputs only): also store the chunk-start states there for
+    ``chunk_bwd(..., saved=True)`` (``dn_chunk_fwd_save``).
     """
     lib = load_library()
     s, N = _shape(q, v, cu_seqlens, chunk)
@@ -150,6 +157,12 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_stat
     _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
     hT = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
+    if save_workspace is not None:
+        _check("dn_chunk_fwd_save", lib.dn_chunk_fwd_save(
+            ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
+            _ptr(cu_seqlens), _ptr(o), _ptr(hT), _ptr(save_workspace), save_workspace.numel(),
+            _stream(dev)))
+        return o, hT
     wsb = lib.dn_chunk_fwd_workspace(ctypes.byref(s))
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     _check("dn_chunk_fwd", lib.dn_chunk_fwd(
@@ -159,7 +172,7 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_stat
 
 
 def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 64,
-              workspace: Optional[torch.Tensor] = None, events=None):
+              workspace: Optional[torch.Tensor] = None, events=None, saved: bool = False):
     """Backward pass of ``<dO, o> + <dhT, hT>``.
 
     Returns a dict of float32 gradients dq, dk, dv, dbeta, dg (None without a
@@ -167,7 +180,9 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     may be passed to avoid an allocation per call.  ``events``: four
     ``torch.cuda.Event(enable_timing=True)`` that the library records before
     its first kernel and after the recompute, the state-gradient sweep and the
-    chunk-gradient kernel (``dn_chunk_bwd_events``).
+    chunk-gradient kernel (``dn_chunk_bwd_events``).  ``saved``: skip the
+    recompute and read the states that ``chunk_fwd(..., save_workspace=
+    workspace)`` stored for these inputs (``dn_chunk_bwd_saved``).
     """
     lib = load_library()
     s, N = _shape(q, v, cu_seqlens, chunk)
@@ -190,6 +205,8 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     dg = torch.empty((B, T, H), **f32) if g is not None else None
     dh0 = torch.empty((N, H, Dk, Dv), **f32)
     wsb = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
+    if saved and workspace is None:
+        raise ValueError("saved=True needs the workspace that chunk_fwd filled")
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     ev = None
@@ -200,7 +217,8 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
             if e.cuda_event == 0:  # torch creates the event on its first record
                 e.record(torch.cuda.current_stream(dev))
         ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
-    _check("dn_chunk_bwd", lib.dn_chunk_bwd_events(
+    fn = lib.dn_chunk_bwd_saved if saved else lib.dn_chunk_bwd_events
+    _check("dn_chunk_bwd_saved" if saved else "dn_chunk_bwd", fn(
         ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
         _ptr(cu_seqlens), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),
         _ptr(dg), _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(dev), ev))
@@ -337,12 +355,23 @@ def prologue_bwd(q_in, k_in, b_in, x_in, gate_scale, dq, dk, dbeta, dg=None):
 
 class DeltaRule(torch.autograd.Function):
     """Autograd wrapper: forward by ``chunk_fwd``, backward by ``chunk_bwd``.
-    Gradients are computed in float32 and cast to each input's dtype."""
+    Gradients are computed in float32 and cast to each input's dtype.  For
+    bfloat16 inputs with ``save_states`` the forward pass keeps the bf16 chunk
+    states (d_k d_v per chunk and head) and the backward pass skips their
+    recompute; otherwise the backward pass recomputes them."""
 
     @staticmethod
-    def forward(ctx, q, k, v, beta, g, h0, cu_seqlens):
-        o, hT = chunk_fwd(q, k, v, beta, g, h0, cu_seqlens, output_final_state=True)
+    def forward(ctx, q, k, v, beta, g, h0, cu_seqlens, save_states=True):
+        ws = None
+        if save_states and q.dtype == torch.bfloat16:
+            N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+            ws = torch.empty(max(bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3],
+                                                     v.shape[-1], N, q.dtype), 1),
+                             dtype=torch.uint8, device=q.device)
+        o, hT = chunk_fwd(q, k, v, beta, g, h0, cu_seqlens, output_final_state=True,
+                          save_workspace=ws)
         ctx.save_for_backward(q, k, v, beta, g, h0, cu_seqlens)
+        ctx.ws = ws
         return o, hT
 
     @staticmethod
@@ -350,12 +379,16 @@ class DeltaRule(torch.autograd.Function):
         q, k, v, beta, g, h0, cu = ctx.saved_tensors
         if dO is None:
             dO = torch.zeros(v.shape, dtype=q.dtype, device=q.device)
+        ws, ctx.ws = ctx.ws, None
         gr = chunk_bwd(q, k, v, beta, g, h0, dO.to(q.dtype).contiguous(),
-                       None if dhT is None else dhT.float().contiguous(), cu)
+                       None if dhT is None else dhT.float().contiguous(), cu,
+                       workspace=ws, saved=ws is not None)
         return (gr["dq"].to(q.dtype), gr["dk"].to(k.dtype), gr["dv"].to(v.dtype), gr["dbeta"],
-                gr["dg"], None if h0 is None else gr["dh0"], None)
+                gr["dg"], None if h0 is None else gr["dh0"], None, None)
 
 
-def delta_rule(q, k, v, beta, g=None, h0=None, cu_seqlens=None):
-    """Differentiable chunkwise (gated) delta rule; returns (o, hT)."""
-    return DeltaRule.apply(q, k, v, beta, g, h0, cu_seqlens)
+def delta_rule(q, k, v, beta, g=None, h0=None, cu_seqlens=None, save_states=True):
+    """Differentiable chunkwise (gated) delta rule; returns (o, hT).
+    ``save_states`` keeps the chunk states from the forward pass for the
+    backward pass (bfloat16 inputs) instead of recomputing them."""
+    return DeltaRule.apply(q, k, v, beta, g, h0, cu_seqlens, save_states)

@@ -55,6 +55,131 @@ BwdLayout bwd_layout(const dn_shape *s, bool varlen) {
 
 dn_status from_hip(hipError_t e) { return e == hipSuccess ? DN_OK : DN_EHIP; }
 
+dn::FwdParams fwd_params(const dn_shape *s, const void *q, const void *k, const void *v,
+                         const float *beta, const float *g, const float *h0, const int32_t *cu) {
+  dn::FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.beta = beta;
+  p.g = g;
+  p.h0 = h0;
+  p.cu = cu;
+  p.B = s->B;
+  p.T = s->T;
+  p.H = s->H;
+  p.DV = s->Dv;
+  p.N = s->n_seqs;
+  p.NC = (s->T + 63) / 64;
+  p.ntiles = s->Dv / 64;
+  p.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
+  return p;
+}
+
+// Checks shared by the passes that use the backward workspace (bf16 only).
+dn_status check_train(const dn_shape *s, const int32_t *cu, const void *q, const void *k, const void *v,
+                      const float *beta) {
+  dn_status st = check_shape(s, cu);
+  if (st != DN_OK) return st;
+  if (s->dtype != DN_BF16) return DN_EUNSUPPORTED;  // the backward kernels are bf16
+  if (s->T > 0) {
+    if (!q || !k || !v || !beta) return DN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return DN_EINVAL;
+  }
+  return DN_OK;
+}
+
+// Pieces of the backward workspace; builds the packed-sequence chunk table
+// (varlen) on `stream`.
+struct TrainWs {
+  bf16 *states, *dstates;
+  int32_t *chunk_base, *chunk_seq;
+  int64_t nchunks;
+};
+
+dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream, TrainWs &w) {
+  const bool varlen = cu != nullptr;
+  // the workspace query cannot see cu_seqlens, so it sizes for the varlen bound
+  const BwdLayout L = bwd_layout(s, varlen || s->B == 1);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return DN_ENOWS;
+  char *ws = static_cast<char *>(workspace);
+  w.nchunks = max_chunks(s, varlen);
+  w.chunk_base = w.chunk_seq = nullptr;
+  if (varlen) {
+    w.chunk_base = reinterpret_cast<int32_t *>(ws + L.table);
+    w.chunk_seq = w.chunk_base + s->n_seqs + 1;
+    hipError_t e = dn::launch_chunk_table(cu, s->n_seqs, w.chunk_base, w.chunk_seq, (int)w.nchunks, stream);
+    if (e != hipSuccess) return DN_EHIP;
+  }
+  w.states = reinterpret_cast<bf16 *>(ws + L.states);
+  w.dstates = reinterpret_cast<bf16 *>(ws + L.dstates);
+  return DN_OK;
+}
+
+// The backward pass.  With `recompute` false it reads the chunk-start states
+// that the saving forward pass left in the workspace instead of recomputing
+// them.
+dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v, const float *beta,
+                  const float *g, const float *h0, const int32_t *cu_seqlens, const void *dO,
+                  const float *dhT, float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
+                  bool recompute) {
+  dn_status st = check_train(s, cu_seqlens, q, k, v, beta);
+  if (st != DN_OK) return st;
+  if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
+  if (s->T > 0) {
+    if (!dO || !dq || !dk || !dv || !dbeta) return DN_EINVAL;
+    if (!aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return DN_EINVAL;
+  }
+  TrainWs w;
+  st = train_ws(s, cu_seqlens, workspace, workspace_bytes, stream, w);
+  if (st != DN_OK) return st;
+  if (events && hipEventRecord(events[0], stream) != hipSuccess) return DN_EHIP;
+
+  // 1. forward sweep that stores every chunk-start state
+  dn::FwdParams fp = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
+  fp.states = w.states;
+  fp.chunk_base = w.chunk_base;
+  if (recompute) {
+    hipError_t e = dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
+    if (e != hipSuccess) return DN_EHIP;
+  }
+  if (events && hipEventRecord(events[1], stream) != hipSuccess) return DN_EHIP;
+
+  // 2. reverse sweep for the state gradients, 3. chunk-parallel token gradients
+  dn::BwdParams bp = {};
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.dO = dO;
+  bp.beta = beta;
+  bp.g = g;
+  bp.dhT = dhT;
+  bp.cu = cu_seqlens;
+  bp.chunk_base = w.chunk_base;
+  bp.chunk_seq = w.chunk_seq;
+  bp.states = w.states;
+  bp.dstates = w.dstates;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dbeta = dbeta;
+  bp.dg = dg;
+  bp.dh0 = dh0;
+  bp.B = s->B;
+  bp.T = s->T;
+  bp.H = s->H;
+  bp.DV = s->Dv;
+  bp.N = s->n_seqs;
+  bp.NC = (s->T + 63) / 64;
+  bp.ntiles = s->Dv / 64;
+  bp.xcd_map = fp.xcd_map;
+  bp.total_chunks = (int)w.nchunks;
+  return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream, events ? events[2] : nullptr,
+                                 events ? events[3] : nullptr));
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,26 +212,9 @@ dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const vo
     if (!q || !k || !v || !beta || !o) return DN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_EINVAL;
   }
-  dn::FwdParams p = {};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.beta = beta;
-  p.g = g;
-  p.h0 = h0;
-  p.cu = cu_seqlens;
+  dn::FwdParams p = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
   p.o = o;
   p.hT = hT;
-  p.states = nullptr;
-  p.chunk_base = nullptr;
-  p.B = s->B;
-  p.T = s->T;
-  p.H = s->H;
-  p.DV = s->Dv;
-  p.N = s->n_seqs;
-  p.NC = (s->T + 63) / 64;
-  p.ntiles = s->Dv / 64;
-  p.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
   return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, false, true, stream));
 }
 
@@ -131,90 +239,35 @@ dn_status dn_chunk_bwd_events(const dn_shape *s, const void *q, const void *k, c
                               float *dk, float *dv, float *dbeta, float *dg, float *dh0,
                               void *workspace, size_t workspace_bytes, hipStream_t stream,
                               hipEvent_t *events) {
-  dn_status st = check_shape(s, cu_seqlens);
+  return bwd_run(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq, dk, dv, dbeta, dg, dh0, workspace,
+                 workspace_bytes, stream, events, true);
+}
+
+dn_status dn_chunk_fwd_save(const dn_shape *s, const void *q, const void *k, const void *v,
+                            const float *beta, const float *g, const float *h0,
+                            const int32_t *cu_seqlens, void *o, float *hT, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  dn_status st = check_train(s, cu_seqlens, q, k, v, beta);
   if (st != DN_OK) return st;
-  if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
-  if (s->dtype != DN_BF16) return DN_EUNSUPPORTED;  // the backward kernels are bf16
-  const bool varlen = cu_seqlens != nullptr;
-  if (s->T > 0) {
-    if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return DN_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) ||
-        !aligned16(dk) || !aligned16(dv))
-      return DN_EINVAL;
-  }
-  // the workspace query cannot see cu_seqlens, so it sizes for the varlen bound
-  const BwdLayout L = bwd_layout(s, varlen || s->B == 1);
-  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return DN_ENOWS;
-  char *ws = static_cast<char *>(workspace);
-  const int64_t nchunks = max_chunks(s, varlen);
-  int32_t *chunk_base = nullptr, *chunk_seq = nullptr;
-  if (varlen) {
-    chunk_base = reinterpret_cast<int32_t *>(ws + L.table);
-    chunk_seq = chunk_base + s->n_seqs + 1;
-    hipError_t e = dn::launch_chunk_table(cu_seqlens, s->n_seqs, chunk_base, chunk_seq,
-                                          (int)nchunks, stream);
-    if (e != hipSuccess) return DN_EHIP;
-  }
-  bf16 *states = reinterpret_cast<bf16 *>(ws + L.states);
-  bf16 *dstates = reinterpret_cast<bf16 *>(ws + L.dstates);
-  if (events && hipEventRecord(events[0], stream) != hipSuccess) return DN_EHIP;
+  if (s->T > 0 && (!o || !aligned16(o))) return DN_EINVAL;
+  TrainWs w;
+  st = train_ws(s, cu_seqlens, workspace, workspace_bytes, stream, w);
+  if (st != DN_OK) return st;
+  dn::FwdParams p = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
+  p.o = o;
+  p.hT = hT;
+  p.states = w.states;
+  p.chunk_base = w.chunk_base;
+  return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, true, true, stream));
+}
 
-  // 1. forward sweep that stores every chunk-start state
-  dn::FwdParams fp = {};
-  fp.q = q;
-  fp.k = k;
-  fp.v = v;
-  fp.beta = beta;
-  fp.g = g;
-  fp.h0 = h0;
-  fp.cu = cu_seqlens;
-  fp.o = nullptr;
-  fp.hT = nullptr;
-  fp.states = states;
-  fp.chunk_base = chunk_base;
-  fp.B = s->B;
-  fp.T = s->T;
-  fp.H = s->H;
-  fp.DV = s->Dv;
-  fp.N = s->n_seqs;
-  fp.NC = (s->T + 63) / 64;
-  fp.ntiles = s->Dv / 64;
-  fp.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
-  hipError_t e = dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
-  if (e != hipSuccess) return DN_EHIP;
-  if (events && hipEventRecord(events[1], stream) != hipSuccess) return DN_EHIP;
-
-  // 2. reverse sweep for the state gradients, 3. chunk-parallel token gradients
-  dn::BwdParams bp = {};
-  bp.q = q;
-  bp.k = k;
-  bp.v = v;
-  bp.dO = dO;
-  bp.beta = beta;
-  bp.g = g;
-  bp.dhT = dhT;
-  bp.cu = cu_seqlens;
-  bp.chunk_base = chunk_base;
-  bp.chunk_seq = chunk_seq;
-  bp.states = states;
-  bp.dstates = dstates;
-  bp.dq = dq;
-  bp.dk = dk;
-  bp.dv = dv;
-  bp.dbeta = dbeta;
-  bp.dg = dg;
-  bp.dh0 = dh0;
-  bp.B = s->B;
-  bp.T = s->T;
-  bp.H = s->H;
-  bp.DV = s->Dv;
-  bp.N = s->n_seqs;
-  bp.NC = (s->T + 63) / 64;
-  bp.ntiles = s->Dv / 64;
-  bp.xcd_map = fp.xcd_map;
-  bp.total_chunks = (int)nchunks;
-  return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream, events ? events[2] : nullptr,
-                                 events ? events[3] : nullptr));
+dn_status dn_chunk_bwd_saved(const dn_shape *s, const void *q, const void *k, const void *v,
+                             const float *beta, const float *g, const float *h0,
+                             const int32_t *cu_seqlens, const void *dO, const float *dhT, float *dq,
+                             float *dk, float *dv, float *dbeta, float *dg, float *dh0, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream, hipEvent_t *events) {
+  return bwd_run(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq, dk, dv, dbeta, dg, dh0, workspace,
+                 workspace_bytes, stream, events, false);
 }
 
 dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,

@@ -130,6 +130,44 @@ dn_status dn_chunk_bwd_events(const dn_shape *s,
                               hipEvent_t *events);
 
 /*
+ * Training forward pass that keeps the chunk states for the backward pass
+ * (the materialising alternative of Parallelizing Linear Transformers...,
+ * page 1, answer Q2: chunk-level states written to HBM in the forward pass,
+ * so that the backward pass need not recompute them).  The same operation,
+ * arguments, outputs and errors as dn_chunk_fwd, bf16 only
+ * (DN_EUNSUPPORTED otherwise), and in addition it writes every chunk-start
+ * state S = h^T in bf16 (and, for packed input, the chunk table) into
+ * `workspace`, which must hold dn_chunk_bwd_workspace(s) bytes
+ * (DN_ENOWS otherwise).  The workspace then belongs to the matching
+ * dn_chunk_bwd_saved call; its contents are opaque.
+ */
+dn_status dn_chunk_fwd_save(const dn_shape *s,
+                            const void *q, const void *k, const void *v,
+                            const float *beta, const float *g, const float *h0,
+                            const int32_t *cu_seqlens,
+                            void *o, float *hT,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward pass from saved states: dn_chunk_bwd_events without the state
+ * recompute.  It reads the chunk-start states that dn_chunk_fwd_save stored
+ * in `workspace`; the caller guarantees that q, k, v, beta, g, h0,
+ * cu_seqlens and the workspace are unchanged since that call and that the
+ * call is ordered after it (same stream, or synchronised); otherwise the
+ * gradients are those of whatever states the workspace holds.  Arguments,
+ * outputs and errors as dn_chunk_bwd_events; events (NULL: none) are recorded
+ * as there, events[0] and events[1] back to back since there is no recompute.
+ */
+dn_status dn_chunk_bwd_saved(const dn_shape *s,
+                             const void *q, const void *k, const void *v,
+                             const float *beta, const float *g, const float *h0,
+                             const int32_t *cu_seqlens,
+                             const void *dO, const float *dhT,
+                             float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream,
+                             hipEvent_t *events);
+
+/*
  * One recurrent (decode) step for B x H independent states: the token update
  * above applied once (Gated DeltaNet review thread, General Response 2: the
  * recurrent step is memory-bound and its cost is set by the state size).

@@ -150,3 +150,34 @@ def test_prologue_validation(lib):
     bad = list(args)
     bad[9] = P(FAKE + 4)  # misaligned dq_in
     assert fb(1, 1, 1, 64, 0, *bad) == DN_EINVAL
+
+
+def fwd_save(lib, s, q=FAKE, o=FAKE, ws=FAKE, wsb=1 << 40):
+    P = ctypes.c_void_p
+    return lib.dn_chunk_fwd_save(ctypes.byref(s), P(q), P(FAKE), P(FAKE), P(FAKE), None, None, None,
+                                 P(o), None, P(ws), wsb, None)
+
+
+def bwd_saved(lib, s, g=None, dg=None, ws=FAKE, wsb=1 << 40):
+    P = ctypes.c_void_p
+    return lib.dn_chunk_bwd_saved(ctypes.byref(s), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(g), None, None,
+                                  P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(dg), None,
+                                  P(ws), wsb, None, None)
+
+
+def test_saved_state_pair_validation(lib):
+    s = shape()
+    need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
+    # the saving forward pass: bf16 only, the backward workspace, the forward's own checks
+    assert fwd_save(lib, shape(dtype=0)) == DN_EUNSUPPORTED
+    assert fwd_save(lib, s, q=None) == DN_EINVAL
+    assert fwd_save(lib, s, o=None) == DN_EINVAL
+    assert fwd_save(lib, s, o=FAKE + 8) == DN_EINVAL
+    assert fwd_save(lib, s, wsb=need - 1) == DN_ENOWS
+    assert fwd_save(lib, s, ws=None) == DN_ENOWS
+    assert fwd_save(lib, shape(chunk=32)) == DN_EUNSUPPORTED
+    # the backward pass from saved states validates as the recomputing one
+    assert bwd_saved(lib, s, g=FAKE, dg=None) == DN_EINVAL
+    assert bwd_saved(lib, s, g=None, dg=FAKE) == DN_EINVAL
+    assert bwd_saved(lib, s, wsb=need - 1) == DN_ENOWS
+    assert bwd_saved(lib, shape(dtype=0)) == DN_EUNSUPPORTED

@@ -22,16 +22,26 @@ def to_dev(x):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
 
 
-def gpu_bwd(x):
+def gpu_bwd(x, saved=False):
+    """Backward pass through dn_chunk_bwd, or (saved) through dn_chunk_fwd_save
+    followed by dn_chunk_bwd_saved on one workspace."""
     d = to_dev(x)
+    ws = None
+    if saved:
+        q, v = d["q"], d["v"]
+        N = q.shape[0] if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
+        ws = torch.empty(dn.bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3],
+                                                v.shape[-1], N), dtype=torch.uint8, device=DEV)
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"],
+                     save_workspace=ws)
     gr = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
-                      d["cu_seqlens"])
+                      d["cu_seqlens"], workspace=ws, saved=saved)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu()) for k, v in gr.items()}
 
 
-def check_bwd(x, oracle_lib, label):
-    gr = gpu_bwd(x)
+def check_bwd(x, oracle_lib, label, saved=False):
+    gr = gpu_bwd(x, saved)
     ref = oracle_lib.bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["dO"], x["dhT"],
                          cu_seqlens=x["cu_seqlens"])
     errs = {}
@@ -124,10 +134,11 @@ def test_autograd_wrapper_matches_entry_points():
     assert torch.equal(q.grad, gr["dq"].to(torch.bfloat16))
 
 
-def test_bwd_full_size_sampled(oracle_lib):
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_bwd_full_size_sampled(oracle_lib, saved):
     sh = synth.WORKLOADS[4]
     x = synth.workload_inputs(4)
-    gr = gpu_bwd(x)
+    gr = gpu_bwd(x, saved)
     for name in NAMES:
         assert torch.isfinite(gr[name]).all(), name
     rng = np.random.default_rng(4)
@@ -147,13 +158,14 @@ def test_bwd_full_size_sampled(oracle_lib):
             assert e <= TOL, (name, e)
 
 
-def test_bwd_varlen_full_size_sampled(oracle_lib):
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_bwd_varlen_full_size_sampled(oracle_lib, saved):
     """Packed workload (8 sequences, 65536 tokens, H=32, d=128) in one call;
     three (sequence, head) pairs of the shorter sequences, which sit after the
     first in the packing and end in partial chunks, against the oracle."""
     sh = synth.WORKLOADS[6]
     x = synth.workload_inputs(6)
-    gr = gpu_bwd(x)
+    gr = gpu_bwd(x, saved)
     for name in NAMES:
         assert torch.isfinite(gr[name]).all(), name
     cu = x["cu_seqlens"].tolist()
@@ -173,3 +185,42 @@ def test_bwd_varlen_full_size_sampled(oracle_lib):
               " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
         for name, e in errs.items():
             assert e <= TOL, (name, e)
+
+
+SAVED_CASES = [
+    # B, T, H, Dk, Dv, gated, h0, lengths
+    (2, 150, 2, 128, 128, True, True, None),
+    (2, 200, 2, 128, 256, False, False, None),
+    (2, 64, 3, 64, 192, True, True, None),
+    (1, 328, 2, 128, 128, True, True, (1, 63, 64, 65, 0, 130, 5)),
+]
+
+
+@pytest.mark.parametrize("cfg", SAVED_CASES, ids=lambda c: "B%dT%dH%dk%dv%d-g%d-h%d-%s" % (
+    c[:7] + ("varlen" if c[7] else "fixed",)))
+def test_saved_states_equal_recompute(oracle_lib, cfg):
+    """dn_chunk_fwd_save writes dn_chunk_fwd's outputs bit for bit and the
+    chunk states the backward's recompute would write, so dn_chunk_bwd_saved
+    returns dn_chunk_bwd's gradients bit for bit; both are within the
+    tolerance of the oracle."""
+    B, T, H, Dk, Dv, gated, h0, lens = cfg
+    sh = Shape(B, T, H, Dk, Dv, torch.bfloat16, gated, h0, backward=True, lengths=lens)
+    x = make_inputs(sh, seed=41 + T)
+    d = to_dev(x)
+    o_ref, hT_ref = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+    N = sh.n_seqs
+    ws = torch.empty(dn.bwd_workspace_bytes(B, T, H, Dk, Dv, N), dtype=torch.uint8, device=DEV)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"],
+                         save_workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(hT, hT_ref)
+    gs = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
+                      d["cu_seqlens"], workspace=ws, saved=True)
+    torch.cuda.synchronize()
+    gs = {k: (None if v is None else v.cpu()) for k, v in gs.items()}
+    gr = check_bwd(x, oracle_lib, "recompute " + str(cfg))
+    for name in NAMES:
+        if gr[name] is None:
+            assert gs[name] is None
+        else:
+            assert torch.equal(gs[name], gr[name]), name

@@ -26,6 +26,9 @@ dn_status check_shape(const dn_shape *s, const int32_t *cu) {
   if (s->dtype == DN_F32 && s->Dk != 64) return DN_EUNSUPPORTED;
   // element offsets are computed in 64-bit, but grid and per-sequence counts are int
   if ((int64_t)s->n_seqs * s->H * (s->Dv / 64) > (int64_t)1 << 30) return DN_EUNSUPPORTED;
+  // the kernels address the rows of one chunk (64 tokens of one head, fp32 at
+  // most) with 32-bit offsets from the chunk's first row
+  if ((int64_t)64 * s->H * (s->Dk > s->Dv ? s->Dk : s->Dv) * 4 > INT32_MAX) return DN_EUNSUPPORTED;
   return DN_OK;
 }
 

@@ -37,7 +37,9 @@
  *   enqueued.  Kernel faults surface at the caller's next synchronisation.
  * - Supported: Dk in {64, 128}; Dv a positive multiple of 64 up to 1024;
  *   chunk == 64; dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
- *   pointers 16-byte aligned.
+ *   pointers 16-byte aligned; 256 H max(Dk, Dv) < 2^31 (the byte span of one
+ *   64-token chunk of fp32 rows, addressed with 32-bit offsets).  Shapes
+ *   outside these limits return DN_EUNSUPPORTED.
  */
 #ifndef DN_H_
 #define DN_H_

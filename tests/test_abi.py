@@ -68,9 +68,16 @@ def bwd(lib, s, g=None, dg=None, ws=FAKE, wsb=1 << 40, cu=None, q=FAKE):
     (dict(chunk=32), DN_EUNSUPPORTED), (dict(Dk=96), DN_EUNSUPPORTED),
     (dict(Dk=256), DN_EUNSUPPORTED), (dict(Dv=48), DN_EUNSUPPORTED),
     (dict(Dv=2048), DN_EUNSUPPORTED), (dict(dtype=0, Dk=128), DN_EUNSUPPORTED),
+    # one chunk's rows must stay within 32-bit byte offsets: 256 H max(Dk, Dv) < 2^31
+    (dict(H=8192, Dv=1024), DN_EUNSUPPORTED), (dict(H=1 << 21, Dk=128, Dv=64), DN_EUNSUPPORTED),
 ])
 def test_fwd_rejects_bad_shapes(lib, kw, code):
     assert fwd(lib, shape(**kw)) == code
+
+
+def test_fwd_accepts_largest_chunk_span(lib):
+    # 256 * 8191 * 1024 < 2^31: accepted by validation, which then fails on the null output
+    assert fwd(lib, shape(H=8191, Dv=1024), o=None) == DN_EINVAL
 
 
 def test_fwd_rejects_null_and_misaligned(lib):

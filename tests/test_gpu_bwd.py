@@ -65,6 +65,8 @@ CASES = [
     (2, 64, 3, 64, 192, True, True),
     (1, 1, 2, 128, 128, True, True),
     (1, 129, 9, 128, 64, True, False),
+    (1, 130, 1, 128, 1024, True, True),   # the largest d_v, ragged tail
+    (2, 70, 1, 64, 1024, False, True),
 ]
 
 

@@ -52,6 +52,8 @@ SMALL = [
     (3, 64, 1, 128, 64, torch.bfloat16, True, False),
     (1, 1, 2, 128, 128, torch.bfloat16, True, True),
     (1, 65, 9, 128, 128, torch.bfloat16, True, True),   # N*H not a multiple of 8
+    (1, 130, 1, 128, 1024, torch.bfloat16, True, True),  # the largest d_v, ragged tail
+    (1, 100, 1, 64, 1024, torch.float32, True, True),    # the largest d_v in fp32
 ]
 
 
@@ -167,6 +169,7 @@ def test_fwd_canary_no_out_of_bounds_writes():
     (3, 2, 64, 64, torch.float32, False),
     (5, 3, 128, 256, torch.bfloat16, True),
     (2, 2, 64, 192, torch.float32, True),
+    (2, 1, 128, 1024, torch.bfloat16, True),     # the largest d_v
 ])
 def test_step_parity(oracle_lib, B, H, Dk, Dv, dtype, gated):
     x = synth.decode_inputs(B, H, Dk, Dv, dtype, gated)

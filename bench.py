@@ -33,6 +33,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 # known size (commands and raw counts under profiles/); it describes the kernel as
 # built when the counters were taken
 CHUNK_GRAD_TRAFFIC_W4 = 1511.6e6
+# the same for the forward kernel at the gated forward-only workload (B=4 T=4096
+# H=16 dk=128 dv=256): 294.0 MB read + 142.6 MB written
+FWD_TRAFFIC_W3 = 436.6e6
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
 
 
@@ -217,7 +220,8 @@ def main():
     else:
         kname, kus, kbytes = "dn::fwd_bf16_kernel", stage_us["fwd"], workload_bytes(sh, False)
     achieved = kbytes / (kus * 1e-6) / 1e9
-    traffic = CHUNK_GRAD_TRAFFIC_W4 if (backward and wid == 4) else None
+    traffic = (CHUNK_GRAD_TRAFFIC_W4 if (backward and wid == 4) else
+               FWD_TRAFFIC_W3 if (wid == 3 and not args.prologue and not longhorn) else None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kname, "kernel_us": round(kus, 2), "bytes_per_launch": kbytes}

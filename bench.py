@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--workload", default="4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the probes of the machine's own peaks (HBM copy bandwidth, a bf16 "
+                         "MFMA loop, the shader clock) reported beside the vendor figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy a 512 MiB fp32 tensor once (torch copy_): "
                          "the kernel of known size that calibrates rocprofv3 byte counters")
@@ -250,6 +253,12 @@ def main():
         "step_gbs": round(workload_bytes(sh, backward) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 2) for k, v in stage_us.items()},
     }
+    if not args.no_measured_peaks:
+        mp = measured_peaks(torch, dev, stream)
+        if mp is not None:
+            out["measured_peaks"] = mp
+            roofline["frac_of_measured"] = round(achieved / mp["hbm_copy_GBs"], 4)
+            out["mfma_frac_of_measured"] = round(step_tflops / mp["mfma_bf16_TFs"], 4)
     if args.copy_calibration:
         a = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
         b = torch.empty_like(a)
@@ -264,6 +273,62 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds, args.variant)
     print(json.dumps(out), flush=True)
+
+
+def measured_peaks(torch, dev, stream):
+    """The machine's own peaks, measured after the timed steps: HBM bandwidth of
+    a 1 GiB device copy (bytes read + written over time), the bf16 rate of a
+    plain MFMA loop (16x16x32 MFMAs on registers, four waves per SIMD) and the
+    shader clock (a wave spinning on the clock counter, against HIP events)."""
+    import ctypes
+    path = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
+    if not os.path.exists(path):
+        print("measured peaks skipped: %s is not built" % path, file=sys.stderr)
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dnp_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dnp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.dnp_mfma_loop_flops.restype = ctypes.c_double
+    lib.dnp_clock.argtypes = [ctypes.c_ulonglong, ctypes.c_void_p, ctypes.c_void_p]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    a = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    t_copy = timed(lambda: b.copy_(a), 5)
+    copy_gbs = 2 * a.numel() * 4 / t_copy / 1e9
+    del a, b
+    grid, iters = 256 * 4, 2000
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+
+    def mfma():
+        if lib.dnp_mfma_loop(grid, iters, ctypes.c_void_p(sink.data_ptr()), sp) != 0:
+            raise RuntimeError("dnp_mfma_loop failed")
+    t_mfma = timed(mfma, 3)
+    mfma_tfs = lib.dnp_mfma_loop_flops(grid, iters) / t_mfma / 1e12
+    cyc = torch.zeros(1, dtype=torch.int64, device=dev)
+    want = 20_000_000
+
+    def clock():
+        if lib.dnp_clock(want, ctypes.c_void_p(cyc.data_ptr()), sp) != 0:
+            raise RuntimeError("dnp_clock failed")
+    t_clock = timed(clock, 1)
+    sclk_mhz = int(cyc.item()) / t_clock / 1e6
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "mfma_bf16_TFs": round(mfma_tfs, 1),
+            "sclk_MHz": round(sclk_mhz, 1),
+            "how": "1 GiB fp32 device copy (read + write bytes); 16x16x32 bf16 MFMA loop on "
+                   "registers, 1024 workgroups x 4 waves; one wave spinning %d shader-clock "
+                   "cycles against HIP events" % want}
 
 
 def cpu_baseline(x, sh, backward, budget_s, variant="delta"):

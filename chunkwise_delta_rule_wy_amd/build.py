@@ -9,6 +9,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdn.so")
+# the machine probes of the benchmark (measured MFMA rate, shader clock) live in a
+# library of their own
+PROBE_LIB = os.path.join(HERE, "libdnprobe.so")
+PROBE_SOURCES = ["dn_probe.hip"]
+# per-source flags: the probe's MFMA loop keeps its accumulators in VGPRs (with
+# AGPR accumulators the register allocator shuffles them between rounds)
+EXTRA_FLAGS = {"dn_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["dn_api.hip", "dn_fwd.hip", "dn_fwd_f32.hip", "dn_bwd.hip", "dn_scan.hip", "dn_bwd_chunk.hip", "dn_step.hip", "dn_longhorn.hip", "dn_prologue.hip"]
 
 HIPCC_FLAGS = [
@@ -26,14 +33,21 @@ def _hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libdn.so next to this file."""
+    """Compile every HIP source and link libdn.so (and libdnprobe.so) next to
+    this file."""
+    _link(SOURCES, LIB, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _link(sources, lib, verbose):
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [_hipcc()] + HIPCC_FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         msg = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
                         if "not a recognized feature" not in ln)
@@ -42,13 +56,12 @@ def build(verbose: bool = False) -> str:
         if verbose and msg.strip():
             print(msg, file=sys.stderr)
         objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -188,3 +188,20 @@ def test_saved_state_pair_validation(lib):
     assert bwd_saved(lib, s, g=None, dg=FAKE) == DN_EINVAL
     assert bwd_saved(lib, s, wsb=need - 1) == DN_ENOWS
     assert bwd_saved(lib, shape(dtype=0)) == DN_EUNSUPPORTED
+
+
+def test_probe_library_exports_and_validates():
+    # the benchmark's machine probes: own library, host-side argument checks
+    path = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
+    plib = ctypes.CDLL(path)
+    for name in ("dnp_mfma_loop", "dnp_mfma_loop_flops", "dnp_clock"):
+        assert hasattr(plib, name), name
+    plib.dnp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    plib.dnp_mfma_loop_flops.restype = ctypes.c_double
+    assert plib.dnp_mfma_loop_flops(2, 3) == 2 * 4 * 3 * 16 * 16384
+    plib.dnp_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert plib.dnp_mfma_loop(0, 1, ctypes.c_void_p(FAKE), None) == -1
+    assert plib.dnp_mfma_loop(1, 1, None, None) == -1
+    plib.dnp_clock.argtypes = [ctypes.c_ulonglong, ctypes.c_void_p, ctypes.c_void_p]
+    assert plib.dnp_clock(0, ctypes.c_void_p(FAKE), None) == -1
+    assert plib.dnp_clock(1 << 33, ctypes.c_void_p(FAKE), None) == -1

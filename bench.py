@@ -96,6 +96,10 @@ def main():
     ap.add_argument("--workload", default="4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed steps, this many more steps each preceded by a 1 GiB "
+                         "write that evicts the L2s and the 256 MB Infinity Cache; their per-kernel "
+                         "event times are reported as kernel_us_cold (median, min)")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the probes of the machine's own peaks (HBM copy bandwidth, a bf16 "
                          "MFMA loop, the shader clock) reported beside the vendor figures")
@@ -143,7 +147,7 @@ def main():
     # (torch's current stream, which the binding hands to the library)
     stream = torch.cuda.current_stream(dev)
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    nev = max(args.steps, 1)
+    nev = max(args.steps, 1) + max(args.cold_steps, 0)
     fev = [(mk(), mk()) for _ in range(nev)]
     bev = [[mk() for _ in range(4)] for _ in range(nev)] if backward else None
 
@@ -203,20 +207,39 @@ def main():
     tokens = sh.B * sh.T
     value = tokens / (ms_per_step * 1e-3)
 
-    # per-kernel device time, averaged over the timed steps
-    avg = lambda pairs: sum(a.elapsed_time(b) for a, b in pairs) * 1e3 / len(pairs)
-    stage_us = {"fwd": avg(fev[:args.steps])}
-    if backward:
-        for j, name in enumerate(("recompute", "state_grad_scan", "chunk_grad")):
-            if j == 0 and saved:
-                continue  # the forward pass stored the states
-            stage_us[name] = avg([(e[j], e[j + 1]) for e in bev[:args.steps]])
-        if longhorn:
-            stage_us["longhorn_eps_bwd"] = avg(lev[:args.steps])
+    # cold steps: a 1 GiB write before each evicts what the previous step left in
+    # the caches; they are timed by their events only, outside the timed region
+    cold = range(args.steps, args.steps + max(args.cold_steps, 0))
+    if len(cold):
+        scratch = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+        for i in cold:
+            scratch.fill_(float(i))
+            step(i)
+        torch.cuda.synchronize()
+        del scratch
+
+    def stage_times(idx):
+        """Per-kernel device times (us) of the steps in idx, from their events."""
+        us = lambda pairs: [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        t = {"fwd": us([fev[i] for i in idx])}
+        if backward:
+            for j, name in enumerate(("recompute", "state_grad_scan", "chunk_grad")):
+                if j == 0 and saved:
+                    continue  # the forward pass stored the states
+                t[name] = us([(bev[i][j], bev[i][j + 1]) for i in idx])
+            if longhorn:
+                t["longhorn_eps_bwd"] = us([lev[i] for i in idx])
+            if args.prologue:
+                t["prologue_bwd"] = us([pbev[i] for i in idx])
         if args.prologue:
-            stage_us["prologue_bwd"] = avg(pbev[:args.steps])
-    if args.prologue:
-        stage_us["prologue"] = avg(pev[:args.steps])
+            t["prologue"] = us([pev[i] for i in idx])
+        return t
+
+    # per-kernel device time, averaged over the timed steps
+    warm_t = stage_times(range(args.steps))
+    stage_us = {k: sum(v) / len(v) for k, v in warm_t.items()}
+    med = lambda v: sorted(v)[len(v) // 2]
+    cold_t = stage_times(cold) if len(cold) else {}
     flops = fwd_flops(sh) + (bwd_flops(sh) if backward else 0.0)
     if backward:
         kname, kus, kbytes = "dn::bwd_chunk_kernel", stage_us["chunk_grad"], chunk_grad_bytes(sh)
@@ -252,7 +275,11 @@ def main():
         "mfma_frac": round(step_tflops / MFMA_BF16_PEAK_TFS, 4),
         "step_gbs": round(workload_bytes(sh, backward) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "kernel_us_median_min": {k: [round(med(v), 2), round(min(v), 2)] for k, v in warm_t.items()},
     }
+    if cold_t:
+        out["kernel_us_cold"] = {k: {"median": round(med(v), 2), "min": round(min(v), 2)}
+                                 for k, v in cold_t.items()}
     if not args.no_measured_peaks:
         mp = measured_peaks(torch, dev, stream)
         if mp is not None:

@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--workload", default="4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--chunk", type=int, choices=(32, 64), default=64,
+                    help="chunk length of the forward-only workloads (the training pair is 64)")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="after the timed steps, this many more steps each preceded by a 1 GiB "
                          "write that evicts the L2s and the 256 MB Infinity Cache; their per-kernel "
@@ -153,6 +155,9 @@ def main():
 
     longhorn = args.variant == "longhorn"
     saved = backward and args.bwd_mode == "saved"
+    if backward and args.chunk != 64:
+        print("the backward pass runs 64-token chunks only", file=sys.stderr)
+        sys.exit(2)
     lev = [(mk(), mk()) for _ in range(nev)]
 
     pev = [(mk(), mk()) for _ in range(nev)]
@@ -170,7 +175,7 @@ def main():
         if i is not None:
             fev[i][0].record(stream)
         beta = dn.longhorn_eps(k, b0) if longhorn else b0
-        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], d["cu_seqlens"],
+        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], d["cu_seqlens"], chunk=args.chunk,
                              save_workspace=ws if saved else None)
         if i is not None:
             fev[i][1].record(stream)
@@ -244,10 +249,12 @@ def main():
     if backward:
         kname, kus, kbytes = "dn::bwd_chunk_kernel", stage_us["chunk_grad"], chunk_grad_bytes(sh)
     else:
-        kname, kus, kbytes = "dn::fwd_bf16_kernel", stage_us["fwd"], workload_bytes(sh, False)
+        kname = "dn::fwd_bf16_kernel" if args.chunk == 64 else "dn::fwd32_kernel"
+        kus, kbytes = stage_us["fwd"], workload_bytes(sh, False)
     achieved = kbytes / (kus * 1e-6) / 1e9
     traffic = (CHUNK_GRAD_TRAFFIC_W4 if (backward and wid == 4) else
-               FWD_TRAFFIC_W3 if (wid == 3 and not args.prologue and not longhorn) else None)
+               FWD_TRAFFIC_W3 if (wid == 3 and args.chunk == 64 and not args.prologue and not longhorn)
+               else None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kname, "kernel_us": round(kus, 2), "bytes_per_launch": kbytes}
@@ -267,7 +274,7 @@ def main():
         "dtype": "bf16" if sh.dtype == torch.bfloat16 else "f32",
         "data": "synthetic (seeded, L2-normalised q/k, sigmoid beta, -softplus*0.1 gate)",
         "config": {"workload": synth.WORKLOAD_NAMES[wid], "B": sh.B, "T": sh.T, "H": sh.H,
-                   "Dk": sh.Dk, "Dv": sh.Dv, "chunk": 64, "passes": "fwd+bwd" if backward else "fwd",
+                   "Dk": sh.Dk, "Dv": sh.Dv, "chunk": args.chunk, "passes": "fwd+bwd" if backward else "fwd",
                    "n_seqs": sh.n_seqs, "variant": args.variant, "prologue": args.prologue,
                    "bwd_mode": args.bwd_mode if backward else None},
         "roofline": roofline,

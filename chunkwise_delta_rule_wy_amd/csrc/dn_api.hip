@@ -10,7 +10,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t esize(int dtype) { return dtype == DN_BF16 ? 2 : 4; }
 
-dn_status check_shape(const dn_shape *s, const int32_t *cu) {
+// chunk32: the forward pass also takes 32-token chunks (bf16 inputs)
+dn_status check_shape(const dn_shape *s, const int32_t *cu, bool chunk32 = false) {
   if (!s) return DN_EINVAL;
   if (s->B <= 0 || s->T < 0 || s->H <= 0 || s->Dk <= 0 || s->Dv <= 0 || s->n_seqs <= 0)
     return DN_EINVAL;
@@ -20,7 +21,7 @@ dn_status check_shape(const dn_shape *s, const int32_t *cu) {
   } else if (s->n_seqs != s->B) {
     return DN_EINVAL;
   }
-  if (s->chunk != 64) return DN_EUNSUPPORTED;
+  if (s->chunk != 64 && !(chunk32 && s->chunk == 32 && s->dtype == DN_BF16)) return DN_EUNSUPPORTED;
   if (s->Dk != 64 && s->Dk != 128) return DN_EUNSUPPORTED;
   if (s->Dv % 64 != 0 || s->Dv > 1024) return DN_EUNSUPPORTED;
   if (s->dtype == DN_F32 && s->Dk != 64) return DN_EUNSUPPORTED;
@@ -207,7 +208,7 @@ dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const vo
                        const float *beta, const float *g, const float *h0,
                        const int32_t *cu_seqlens, void *o, float *hT, void *workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  dn_status st = check_shape(s, cu_seqlens);
+  dn_status st = check_shape(s, cu_seqlens, true);
   if (st != DN_OK) return st;
   (void)workspace;
   (void)workspace_bytes;
@@ -218,6 +219,7 @@ dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const vo
   dn::FwdParams p = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
   p.o = o;
   p.hT = hT;
+  if (s->chunk == 32) return from_hip(dn::launch_fwd_c32(p, s->Dk, stream));
   return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, false, true, stream));
 }
 

@@ -103,6 +103,8 @@ size_t fwd_smem_bytes(int dtype, int DK);
 size_t fwd_ref_smem_bytes(int dtype, int DK);
 hipError_t launch_fwd(const FwdParams &p, int dtype, int DK, bool store_states, bool write_o,
                       hipStream_t stream);
+// the forward pass with 32-token chunks (bf16)
+hipError_t launch_fwd_c32(const FwdParams &p, int DK, hipStream_t stream);
 hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_states,
                           bool write_o, hipStream_t stream);
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);

@@ -36,7 +36,8 @@
  * - Validation happens on the host before any launch; on error nothing is
  *   enqueued.  Kernel faults surface at the caller's next synchronisation.
  * - Supported: Dk in {64, 128}; Dv a positive multiple of 64 up to 1024;
- *   chunk == 64; dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
+ *   chunk == 64 (dn_chunk_fwd also takes chunk == 32 for DN_BF16 inputs: the
+ *   same result with 32-token chunks); dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
  *   pointers 16-byte aligned; 256 H max(Dk, Dv) < 2^31 (the byte span of one
  *   64-token chunk of fp32 rows, addressed with 32-bit offsets).  Shapes
  *   outside these limits return DN_EUNSUPPORTED.
@@ -67,7 +68,7 @@ typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
 typedef struct {
     int32_t B, T, H, Dk, Dv;
     int32_t n_seqs;
-    int32_t chunk;   /* chunk length; 64 */
+    int32_t chunk;   /* chunk length: 64 (32 also for the bf16 forward pass) */
     int32_t dtype;   /* dn_dtype of q, k, v, o, dO */
 } dn_shape;
 

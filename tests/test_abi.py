@@ -65,7 +65,8 @@ def bwd(lib, s, g=None, dg=None, ws=FAKE, wsb=1 << 40, cu=None, q=FAKE):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), DN_EINVAL), (dict(H=0), DN_EINVAL), (dict(T=-1), DN_EINVAL),
     (dict(Dk=0), DN_EINVAL), (dict(dtype=7), DN_EINVAL), (dict(n_seqs=3), DN_EINVAL),
-    (dict(chunk=32), DN_EUNSUPPORTED), (dict(Dk=96), DN_EUNSUPPORTED),
+    (dict(chunk=16), DN_EUNSUPPORTED), (dict(chunk=32, dtype=0), DN_EUNSUPPORTED),
+    (dict(chunk=128), DN_EUNSUPPORTED), (dict(Dk=96), DN_EUNSUPPORTED),
     (dict(Dk=256), DN_EUNSUPPORTED), (dict(Dv=48), DN_EUNSUPPORTED),
     (dict(Dv=2048), DN_EUNSUPPORTED), (dict(dtype=0, Dk=128), DN_EUNSUPPORTED),
     # one chunk's rows must stay within 32-bit byte offsets: 256 H max(Dk, Dv) < 2^31
@@ -78,6 +79,12 @@ def test_fwd_rejects_bad_shapes(lib, kw, code):
 def test_fwd_accepts_largest_chunk_span(lib):
     # 256 * 8191 * 1024 < 2^31: accepted by validation, which then fails on the null output
     assert fwd(lib, shape(H=8191, Dv=1024), o=None) == DN_EINVAL
+
+
+def test_fwd_takes_32_token_chunks_in_bf16(lib):
+    # accepted by validation (which then fails on the null output)
+    assert fwd(lib, shape(chunk=32), o=None) == DN_EINVAL
+    assert fwd_save(lib, shape(chunk=32)) == DN_EUNSUPPORTED  # the training pair is 64-token
 
 
 def test_fwd_rejects_null_and_misaligned(lib):
@@ -99,6 +106,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, s, wsb=need - 1) == DN_ENOWS
     assert bwd(lib, s, ws=None) == DN_ENOWS
     assert bwd(lib, shape(chunk=128)) == DN_EUNSUPPORTED
+    assert bwd(lib, shape(chunk=32)) == DN_EUNSUPPORTED  # 32-token chunks: forward only
 
 
 def test_bwd_workspace_covers_varlen_bound(lib):

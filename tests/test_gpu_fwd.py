@@ -231,3 +231,68 @@ def test_fwd_full_size_sampled(oracle_lib, wid):
         eh = rel_l2(hT[n, h], ho[0, 0])
         print("workload %d pair (%d,%d) rel-L2 o %.3e hT %.3e" % (wid, n, h, eo, eh), flush=True)
         assert eo <= TOL[sh.dtype] and eh <= TOL[sh.dtype]
+
+
+# ----------------------------------------------------------- 32-token chunks
+C32_CASES = [
+    # B, T, H, Dk, Dv, gated, h0
+    (2, 200, 3, 128, 128, True, True),
+    (1, 31, 2, 64, 64, False, False),
+    (1, 33, 2, 128, 256, True, True),
+    (3, 64, 1, 128, 64, False, True),
+    (1, 1, 2, 128, 128, True, True),
+    (2, 95, 2, 64, 192, True, False),
+    (1, 130, 1, 128, 1024, True, True),
+]
+
+
+@pytest.mark.parametrize("cfg", C32_CASES, ids=lambda c: "B%dT%dH%dk%dv%d-g%d-h%d" % c)
+def test_fwd_chunk32_parity(oracle_lib, cfg):
+    """The 32-token-chunk forward kernel against the oracle (the chunk size does
+    not change the result beyond rounding)."""
+    B, T, H, Dk, Dv, gated, h0 = cfg
+    sh = Shape(B, T, H, Dk, Dv, torch.bfloat16, gated, h0)
+    x = make_inputs(sh, seed=300 + T + Dv)
+    d = to_dev(x)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], chunk=32)
+    torch.cuda.synchronize()
+    oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"])
+    eo, eh = rel_l2(o.cpu(), oo), rel_l2(hT.cpu(), ho)
+    print("chunk 32 %s rel-L2 o %.3e hT %.3e" % (cfg, eo, eh), flush=True)
+    assert eo <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16], (eo, eh)
+
+
+def test_fwd_chunk32_varlen_ragged(oracle_lib):
+    lens = (1, 31, 32, 33, 0, 100, 5)
+    sh = Shape(1, sum(lens), 2, 128, 128, torch.bfloat16, True, True, lengths=lens)
+    x = make_inputs(sh, seed=333)
+    d = to_dev(x)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"], chunk=32)
+    torch.cuda.synchronize()
+    oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["cu_seqlens"])
+    eo, eh = rel_l2(o.cpu(), oo), rel_l2(hT.cpu(), ho)
+    print("chunk 32 varlen rel-L2 o %.3e hT %.3e" % (eo, eh), flush=True)
+    assert eo <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16], (eo, eh)
+    # the empty sequence passes its state through
+    assert torch.equal(hT[4].cpu(), x["h0"][4])
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_fwd_chunk32_full_size_sampled(oracle_lib, wid):
+    """The forward workloads at full size with 32-token chunks: three
+    (batch, head) pairs against the oracle."""
+    sh = synth.WORKLOADS[wid]
+    x = synth.workload_inputs(wid)
+    d = to_dev(x)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], chunk=32)
+    torch.cuda.synchronize()
+    o, hT = o.cpu(), hT.cpu()
+    rng = np.random.default_rng(32 + wid)
+    for idx in rng.choice(sh.B * sh.H, size=3, replace=False):
+        b, h = int(idx) // sh.H, int(idx) % sh.H
+        sl = lambda t: None if t is None else t[b:b + 1, :, h:h + 1].contiguous()
+        st = lambda t: None if t is None else t[b:b + 1, h:h + 1].contiguous()
+        oo, ho = oracle_lib.fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["g"]), st(x["h0"]))
+        eo, eh = rel_l2(o[b:b + 1, :, h:h + 1], oo), rel_l2(hT[b:b + 1, h:h + 1], ho)
+        print("chunk 32 workload %d pair (%d,%d) rel-L2 o %.3e hT %.3e" % (wid, b, h, eo, eh), flush=True)
+        assert eo <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16], (eo, eh)

@@ -1,5 +1,6 @@
-// Machine probes for the benchmark's roofline: the bf16 matrix-core rate a
-// plain MFMA loop reaches, and the shader clock.  Built into its own library
+// Machine probes for the benchmark's roofline: the HBM bandwidth a plain
+// streaming copy reaches, the bf16 matrix-core rate a plain MFMA loop reaches,
+// and the shader clock.  Built into its own library
 // (libdnprobe.so), apart from the operation's library; bench.py times the
 // launches with HIP events on the stream it passes.
 #include <hip/hip_runtime.h>
@@ -52,9 +53,36 @@ __global__ __launch_bounds__(64) void clock_kernel(unsigned long long cycles, un
   if (threadIdx.x == 0) out[0] = t - t0;
 }
 
+// Streaming copy: each thread moves 16-byte units in a grid-stride loop, four
+// loads in flight before their stores.
+__global__ __launch_bounds__(PROBE_THREADS) void copy_kernel(const uint4 *__restrict__ src,
+                                                            uint4 *__restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * PROBE_THREADS;
+  size_t i = (size_t)blockIdx.x * PROBE_THREADS + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Enqueues a device copy of `bytes` (a multiple of 16; both pointers 16-byte
+// aligned) with `grid` workgroups of 256 threads.  Returns 0, -1 for bad
+// arguments, or the HIP error code of the launch.
+int dnp_copy(const void *src, void *dst, size_t bytes, int grid, hipStream_t stream) {
+  if (!src || !dst || grid <= 0 || bytes % 16 != 0 || ((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return -1;
+  if (bytes == 0) return 0;
+  hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(PROBE_THREADS), 0, stream, static_cast<const uint4 *>(src),
+                     static_cast<uint4 *>(dst), bytes / 16);
+  return (int)hipGetLastError();
+}
 
 // Flops one dnp_mfma_loop launch performs (grid workgroups of four waves).
 double dnp_mfma_loop_flops(int grid, int iters) {

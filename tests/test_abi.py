@@ -202,7 +202,7 @@ def test_probe_library_exports_and_validates():
     # the benchmark's machine probes: own library, host-side argument checks
     path = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
     plib = ctypes.CDLL(path)
-    for name in ("dnp_mfma_loop", "dnp_mfma_loop_flops", "dnp_clock"):
+    for name in ("dnp_mfma_loop", "dnp_mfma_loop_flops", "dnp_clock", "dnp_copy"):
         assert hasattr(plib, name), name
     plib.dnp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     plib.dnp_mfma_loop_flops.restype = ctypes.c_double
@@ -213,3 +213,8 @@ def test_probe_library_exports_and_validates():
     plib.dnp_clock.argtypes = [ctypes.c_ulonglong, ctypes.c_void_p, ctypes.c_void_p]
     assert plib.dnp_clock(0, ctypes.c_void_p(FAKE), None) == -1
     assert plib.dnp_clock(1 << 33, ctypes.c_void_p(FAKE), None) == -1
+    plib.dnp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    assert plib.dnp_copy(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 24, 1, None) == -1  # not 16-byte units
+    assert plib.dnp_copy(ctypes.c_void_p(FAKE + 8), ctypes.c_void_p(FAKE), 32, 1, None) == -1
+    assert plib.dnp_copy(None, ctypes.c_void_p(FAKE), 32, 1, None) == -1
+    assert plib.dnp_copy(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 0, 1, None) == 0  # nothing launched

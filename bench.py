@@ -366,11 +366,25 @@ def measured_peaks(torch, dev, stream):
     t_clock = timed(clock, 1)
     sclk_mhz = int(cyc.item()) / t_clock / 1e6
     return {"hbm_copy_GBs": round(copy_gbs, 1), "mfma_bf16_TFs": round(mfma_tfs, 1),
-            "sclk_MHz": round(sclk_mhz, 1),
+            "sclk_MHz": round(sclk_mhz, 1), "mclk_MHz": memory_clock_mhz(),
             "how": "1 GiB device copy, the faster of a streaming copy kernel and torch copy_ "
                    "(read + write bytes); 16x16x32 bf16 MFMA loop on "
                    "registers, 1024 workgroups x 4 waves; one wave spinning %d shader-clock "
                    "cycles against HIP events" % want}
+
+
+def memory_clock_mhz():
+    """The HBM clock that rocm-smi reports for the first GPU (None if it cannot
+    be read); HBM3E at 2000 MHz is the part's 8 TB/s."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        m = re.search(r'"mclk clock speed:":\s*"\((\d+)\s*Mhz\)"', r.stdout)
+        return int(m.group(1)) if m else None
+    except (OSError, subprocess.SubprocessError):
+        return None
 
 
 def cpu_baseline(x, sh, backward, budget_s, variant="delta"):

@@ -263,7 +263,7 @@ def test_p7_varlen_equals_separate_runs_and_decode_steps(oracle_lib):
     assert rel(state[0], hT[n]) < 1e-13
 
 
-@pytest.mark.parametrize("C", [1, 2, 16, 64, 100, 1000])
+@pytest.mark.parametrize("C", [1, 2, 16, 32, 64, 100, 1000])
 @pytest.mark.parametrize("gated", [False, True])
 def test_p8_chunk_algebra_matches_oracle(oracle_lib, C, gated):
     rng = np.random.default_rng(80 + C)
@@ -359,7 +359,7 @@ def test_p10_no_write_gradient_closed_form(oracle_lib):
     np.testing.assert_allclose(gr["dq"], dq_ref, rtol=1e-11, atol=1e-13)
 
 
-@pytest.mark.parametrize("C", [1, 16, 64, 100])
+@pytest.mark.parametrize("C", [1, 16, 32, 64, 100])
 @pytest.mark.parametrize("gated", [False, True])
 def test_p8_chunk_backward_matches_oracle(oracle_lib, C, gated):
     rng = np.random.default_rng(90 + C)

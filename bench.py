@@ -110,7 +110,8 @@ def main():
                          "the kernel of known size that calibrates rocprofv3 byte counters")
     ap.add_argument("--prologue", action="store_true",
                     help="start from the raw draws: the input prologue (L2-normalised q, k; "
-                         "sigmoid beta; -0.1 softplus gate) and its backward run around the passes")
+                         "sigmoid beta; -0.1 softplus gate) runs before the passes and its backward "
+                         "after them (folded into the chunk-gradient kernel with --bwd-mode saved)")
     ap.add_argument("--bwd-mode", choices=("saved", "recompute"), default="saved",
                     help="saved: the forward pass stores the bf16 chunk states and the backward "
                          "pass reads them (dn_chunk_fwd_save + dn_chunk_bwd_saved); recompute: "
@@ -182,16 +183,18 @@ def main():
         if backward:
             # nothing is kept between the passes: the backward recomputes eps
             beta = dn.longhorn_eps(k, b0) if longhorn else b0
+            fused = saved and args.prologue and not longhorn
+            pro = (d["q_in"], d["k_in"], d["x_in"], d["gate_scale"]) if fused else None
             gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"],
                               d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None,
-                              saved=saved)
+                              saved=saved, prologue_inputs=pro)
             if longhorn:
                 if i is not None:
                     lev[i][0].record(stream)
                 gr["dbeta"] = dn.longhorn_eps_bwd(k, b0, gr["dbeta"], gr["dk"])
                 if i is not None:
                     lev[i][1].record(stream)
-            if args.prologue:
+            if args.prologue and not fused:
                 if i is not None:
                     pbev[i][0].record(stream)
                 dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], d["gate_scale"],
@@ -234,7 +237,7 @@ def main():
                 t[name] = us([(bev[i][j], bev[i][j + 1]) for i in idx])
             if longhorn:
                 t["longhorn_eps_bwd"] = us([lev[i] for i in idx])
-            if args.prologue:
+            if args.prologue and not (saved and not longhorn):
                 t["prologue_bwd"] = us([pbev[i] for i in idx])
         if args.prologue:
             t["prologue"] = us([pev[i] for i in idx])

@@ -75,6 +75,9 @@ def load_library():
     lib.dn_chunk_fwd_save.restype = ctypes.c_int
     lib.dn_chunk_bwd_saved.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
     lib.dn_chunk_bwd_saved.restype = ctypes.c_int
+    lib.dn_chunk_bwd_prologue.argtypes = ([S] + [P] * 7 + [P, P] + [P, P, P, ctypes.c_float] + [P] * 6
+                                          + [P, ctypes.c_size_t, P, P])
+    lib.dn_chunk_bwd_prologue.restype = ctypes.c_int
     lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
     lib.dn_recurrent_step.restype = ctypes.c_int
     lib.dn_longhorn_eps.argtypes = [ctypes.c_int32] * 5 + [P] * 3 + [P]
@@ -172,7 +175,8 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_stat
 
 
 def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 64,
-              workspace: Optional[torch.Tensor] = None, events=None, saved: bool = False):
+              workspace: Optional[torch.Tensor] = None, events=None, saved: bool = False,
+              prologue_inputs=None):
     """Backward pass of ``<dO, o> + <dhT, hT>``.
 
     Returns a dict of float32 gradients dq, dk, dv, dbeta, dg (None without a
@@ -183,6 +187,11 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     chunk-gradient kernel (``dn_chunk_bwd_events``).  ``saved``: skip the
     recompute and read the states that ``chunk_fwd(..., save_workspace=
     workspace)`` stored for these inputs (``dn_chunk_bwd_saved``).
+    ``prologue_inputs`` = (q_in, k_in, x_in, gate_scale), with ``saved``: q, k,
+    beta, g are ``prologue``'s outputs for these raw inputs, and the dict holds
+    the gradients of the raw inputs instead: dq_in, dk_in, db_in, dx_in, with
+    dv and dh0 (``dn_chunk_bwd_prologue``: the prologue's backward folded into
+    the chunk-gradient kernel).
     """
     lib = load_library()
     s, N = _shape(q, v, cu_seqlens, chunk)
@@ -217,6 +226,19 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
             if e.cuda_event == 0:  # torch creates the event on its first record
                 e.record(torch.cuda.current_stream(dev))
         ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    if prologue_inputs is not None:
+        if not saved:
+            raise ValueError("prologue_inputs needs saved=True (the states dn_chunk_fwd_save kept)")
+        q_in, k_in, x_in, gate_scale = prologue_inputs
+        _need(q_in, "q_in", q.dtype, (B, T, H, Dk), dev)
+        _need(k_in, "k_in", q.dtype, (B, T, H, Dk), dev)
+        _need(x_in, "x_in", torch.float32, (B, T, H), dev)
+        _check("dn_chunk_bwd_prologue", lib.dn_chunk_bwd_prologue(
+            ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
+            _ptr(cu_seqlens), _ptr(dO), _ptr(dhT), _ptr(q_in), _ptr(k_in), _ptr(x_in),
+            float(gate_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg), _ptr(dh0),
+            _ptr(workspace), workspace.numel(), _stream(dev), ev))
+        return dict(dq_in=dq, dk_in=dk, dv=dv, db_in=dbeta, dx_in=dg, dh0=dh0)
     fn = lib.dn_chunk_bwd_saved if saved else lib.dn_chunk_bwd_events
     _check("dn_chunk_bwd_saved" if saved else "dn_chunk_bwd", fn(
         ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),

@@ -121,14 +121,23 @@ dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t
   return DN_OK;
 }
 
+// Raw inputs of the input prologue, when its backward is folded into the
+// chunk-gradient kernel.
+struct ProIn {
+  const void *q_in = nullptr, *k_in = nullptr;
+  const float *x_in = nullptr;
+  float gate_scale = 0.f;
+};
+
 // The backward pass.  With `recompute` false it reads the chunk-start states
 // that the saving forward pass left in the workspace instead of recomputing
-// them.
+// them; with pro.q_in set the gradient outputs are those of the prologue's
+// raw inputs.
 dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v, const float *beta,
                   const float *g, const float *h0, const int32_t *cu_seqlens, const void *dO,
                   const float *dhT, float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
                   void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
-                  bool recompute) {
+                  bool recompute, const ProIn &pro = ProIn()) {
   dn_status st = check_train(s, cu_seqlens, q, k, v, beta);
   if (st != DN_OK) return st;
   if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
@@ -180,6 +189,10 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   bp.ntiles = s->Dv / 64;
   bp.xcd_map = fp.xcd_map;
   bp.total_chunks = (int)w.nchunks;
+  bp.q_in = pro.q_in;
+  bp.k_in = pro.k_in;
+  bp.x_in = pro.x_in;
+  bp.gate_scale = pro.gate_scale;
   return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream, events ? events[2] : nullptr,
                                  events ? events[3] : nullptr));
 }
@@ -273,6 +286,26 @@ dn_status dn_chunk_bwd_saved(const dn_shape *s, const void *q, const void *k, co
                              size_t workspace_bytes, hipStream_t stream, hipEvent_t *events) {
   return bwd_run(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq, dk, dv, dbeta, dg, dh0, workspace,
                  workspace_bytes, stream, events, false);
+}
+
+dn_status dn_chunk_bwd_prologue(const dn_shape *s, const void *q, const void *k, const void *v,
+                                const float *beta, const float *g, const float *h0,
+                                const int32_t *cu_seqlens, const void *dO, const float *dhT,
+                                const void *q_in, const void *k_in, const float *x_in, float gate_scale,
+                                float *dq_in, float *dk_in, float *dv, float *db_in, float *dx_in,
+                                float *dh0, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t *events) {
+  if ((x_in == nullptr) != (g == nullptr)) return DN_EINVAL;
+  if (s && s->T > 0) {
+    if (!q_in || !k_in || !aligned16(q_in) || !aligned16(k_in)) return DN_EINVAL;
+  }
+  ProIn pro;
+  pro.q_in = q_in ? q_in : q;  // T == 0: nothing is read, but the variant is still the folded one
+  pro.k_in = k_in ? k_in : k;
+  pro.x_in = x_in;
+  pro.gate_scale = gate_scale;
+  return bwd_run(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq_in, dk_in, dv, db_in, dx_in, dh0, workspace,
+                 workspace_bytes, stream, events, false, pro);
 }
 
 dn_status dn_recurrent_step(int32_t B, int32_t H, int32_t Dk, int32_t Dv, int32_t dtype,

@@ -112,7 +112,9 @@ struct BwdKsw {
 };
 
 
-template <int DK, bool GATED>
+// PRO: the input prologue's backward is folded into the stores (the gradients
+// of q_in, k_in, b_in, x_in replace those of q, k, beta, g).
+template <int DK, bool GATED, bool PRO>
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   using LY = BLay<DK>;
   using RS = Res<MODE_CHUNK>;
@@ -487,8 +489,18 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       const float total = lane_val(incl, 63);
       if (r < L) {
         const size_t idx = (row0 + r) * H + h;
-        p.dbeta[idx] = xyr + ld<float>(red + 2304 + 4 * r);
-        if (GATED) p.dg[idx] = total - incl + db;  // sum_{r' >= r} db_r'
+        const float dbeta = xyr + ld<float>(red + 2304 + 4 * r);
+        const float dgr = total - incl + db;  // sum_{r' >= r} db_r'
+        if constexpr (PRO) {
+          // beta = sigmoid(b_in): db_in = dbeta beta (1 - beta); g = -c softplus(x_in):
+          // dx_in = -c sigmoid(x_in) dg
+          const float bt = ld<float>(sb + LY::O_BETA + 4 * r);
+          p.dbeta[idx] = dbeta * bt * (1.f - bt);
+          if (GATED) p.dg[idx] = -p.gate_scale * dgr / (1.f + expf(-p.x_in[idx]));
+        } else {
+          p.dbeta[idx] = dbeta;
+          if (GATED) p.dg[idx] = dgr;
+        }
       }
     }
     mfma_settle();
@@ -623,10 +635,44 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     mfma_settle();
     __syncthreads();  // dPG^T, F^T and the reductions are complete
 
+    // Input prologue (PRO): q = q_in / |q_in| (likewise k) has the gradient
+    // dq_in = (dq - q_in (q_in . dq) / |q_in|^2) / |q_in| (0 for a zero row).
+    // The lane's 32 values of q_in and k_in (row rr, columns 16mt + 4g ..) are
+    // loaded here, ahead of use; dq and dk stay in registers until |q_in|^2 and
+    // q_in . dq are summed over the row's four lanes.  Rows past the chunk read
+    // the chunk's first row (their results are not stored).
+    bf16x4 xq[PRO ? MT : 1], xk[PRO ? MT : 1];
+    if constexpr (PRO) {
+      const size_t xrow = ((row0 + (rr < L ? rr : 0)) * H + h) * (size_t)DK + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        xq[mt] = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(p.q_in) + xrow + 16 * mt);
+        xk[mt] = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(p.k_in) + xrow + 16 * mt);
+      }
+    }
+    // (d - x (x . d) / |x|^2) / |x| over the row, in place
+    auto pro_norm = [&](f32x4 (&d)[MT], const bf16x4 (&x)[PRO ? MT : 1]) {
+      float sq = 0.f, pd = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xv = bf2f(x[mt < (PRO ? MT : 1) ? mt : 0][e]);
+          sq += xv * xv;
+          pd += xv * d[mt][e];
+        }
+      sq = cross_row_sum(sq);
+      pd = cross_row_sum(pd);
+      const float inv = sq > 0.f ? 1.f / sqrtf(sq) : 0.f, c = pd * inv * inv;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[mt][e] = (d[mt][e] - bf2f(x[mt < (PRO ? MT : 1) ? mt : 0][e]) * c) * inv;
+    };
     // dq = diag(gamma) dO h^T + dPG K ;  dk (row part) = diag(w) V' dh^T - diag(gamma beta) Y h^T + F K,
     // as dq^T = gamma dq1^T + K^T dPG^T (and likewise dk): lane (n, g) holds row r = 16rho + n,
     // columns 16mt + 4g .. + 3, written as one 16-byte store
-    f32x4 dkr[MT];
+    f32x4 dkr[MT], dqv[PRO ? MT : 1];
     {
       bf16x8 pgr[2], fr[2];  // B operands: rows r of dPG and F, read transposed from dPG^T, F^T
 #pragma unroll
@@ -650,15 +696,34 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           dk = mma32(dk, kt, fr[kb]);
         }
         dkr[mt] = dk;
-        if (rr < L) *reinterpret_cast<f32x4 *>(dqb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dq;
+        if constexpr (PRO) dqv[mt] = dq;
+        else if (rr < L) *reinterpret_cast<f32x4 *>(dqb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dq;
+      }
+    }
+    if constexpr (PRO) {
+      mfma_settle();
+      pro_norm(dqv, xq);
+      if (rr < L) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dqb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dqv[mt];
       }
     }
     mfma_settle();
     __syncthreads();  // the column part of dk is in LDS
+    if constexpr (PRO) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 dk = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
-      if (rr < L) *reinterpret_cast<f32x4 *>(dkb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dk;
+      for (int mt = 0; mt < MT; ++mt) dkr[mt] = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
+      pro_norm(dkr, xk);
+      if (rr < L) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dkb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dkr[mt];
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 dk = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
+        if (rr < L) *reinterpret_cast<f32x4 *>(dkb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dk;
+      }
     }
   }
 }
@@ -666,7 +731,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 template <int DK>
 hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   const size_t smem = BLay<DK>::TOTAL;
-  auto kern = p.g ? bwd_chunk_kernel<DK, true> : bwd_chunk_kernel<DK, false>;
+  auto kern = p.q_in ? (p.g ? bwd_chunk_kernel<DK, true, true> : bwd_chunk_kernel<DK, false, true>)
+                     : (p.g ? bwd_chunk_kernel<DK, true, false> : bwd_chunk_kernel<DK, false, false>);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;

@@ -34,6 +34,11 @@ struct BwdParams {
   int B, T, H, DV, N, NC;
   int ntiles, xcd_map;
   int total_chunks;           // upper bound of chunks (grid of the chunk-parallel pass)
+  // input prologue folded into the chunk-gradient kernel (q_in set): dq, dk,
+  // dbeta, dg receive the gradients of q_in, k_in, b_in, x_in instead
+  const void *q_in, *k_in;
+  const float *x_in;
+  float gate_scale;
 };
 
 struct StepParams {

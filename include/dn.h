@@ -171,6 +171,31 @@ dn_status dn_chunk_bwd_saved(const dn_shape *s,
                              hipEvent_t *events);
 
 /*
+ * dn_chunk_bwd_saved with the input prologue's backward folded in: for inputs
+ * that dn_prologue prepared (q = q_in / |q_in|, k = k_in / |k_in|,
+ * beta = sigmoid(b_in), g = -gate_scale softplus(x_in)), writes the gradients
+ * of L with respect to the raw inputs instead of those of q, k, beta, g:
+ * dq_in, dk_in [B,T,H,Dk], db_in, dx_in [B,T,H] (fp32; dx_in NULL exactly when
+ * g and x_in are NULL), plus dv and dh0 as dn_chunk_bwd_saved.  The same values
+ * as dn_chunk_bwd_saved followed by dn_prologue_bwd, up to summation order,
+ * without the fp32 dq, dk, dbeta, dg round trip through HBM.  q, k, beta, g are
+ * the prologue's outputs (the recurrence's inputs), q_in and k_in (dtype of q)
+ * its raw inputs; the workspace is the one dn_chunk_fwd_save filled.  Errors as
+ * dn_chunk_bwd_saved, and DN_EINVAL for null or misaligned q_in, k_in (T > 0)
+ * or an x_in/g nullness mismatch.
+ */
+dn_status dn_chunk_bwd_prologue(const dn_shape *s,
+                                const void *q, const void *k, const void *v,
+                                const float *beta, const float *g, const float *h0,
+                                const int32_t *cu_seqlens,
+                                const void *dO, const float *dhT,
+                                const void *q_in, const void *k_in, const float *x_in, float gate_scale,
+                                float *dq_in, float *dk_in, float *dv, float *db_in, float *dx_in,
+                                float *dh0,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t *events);
+
+/*
  * One recurrent (decode) step for B x H independent states: the token update
  * above applied once (Gated DeltaNet review thread, General Response 2: the
  * recurrent step is memory-bound and its cost is set by the state size).

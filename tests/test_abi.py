@@ -218,3 +218,23 @@ def test_probe_library_exports_and_validates():
     assert plib.dnp_copy(ctypes.c_void_p(FAKE + 8), ctypes.c_void_p(FAKE), 32, 1, None) == -1
     assert plib.dnp_copy(None, ctypes.c_void_p(FAKE), 32, 1, None) == -1
     assert plib.dnp_copy(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 0, 1, None) == 0  # nothing launched
+
+
+def test_bwd_prologue_validation(lib):
+    P = ctypes.c_void_p
+    s = shape()
+    f = lib.dn_chunk_bwd_prologue
+    f.argtypes = ([ctypes.c_void_p] + [P] * 7 + [P, P] + [P, P, P, ctypes.c_float] + [P] * 6
+                  + [P, ctypes.c_size_t, P, P])
+
+    def call(g=None, x_in=None, q_in=FAKE, k_in=FAKE, wsb=1 << 40, dtype_shape=s):
+        return f(ctypes.byref(dtype_shape), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(g), None, None,
+                 P(FAKE), None, P(q_in), P(k_in), P(x_in), 0.1, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                 P(g), None, P(FAKE), wsb, None, None)
+    assert call(g=FAKE, x_in=None) == DN_EINVAL      # gate without its raw input
+    assert call(g=None, x_in=FAKE) == DN_EINVAL
+    assert call(q_in=None) == DN_EINVAL
+    assert call(k_in=FAKE + 4) == DN_EINVAL          # misaligned raw keys
+    need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
+    assert call(wsb=need - 1) == DN_ENOWS
+    assert call(dtype_shape=shape(dtype=0)) == DN_EUNSUPPORTED

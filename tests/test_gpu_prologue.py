@@ -75,19 +75,90 @@ def test_prologue_parity(oracle_lib, dtype, Dk, gated):
     assert torch.all(out[0].cpu()[0, 5, 1] == 0) and torch.all(out[1].cpu()[1, 90, 2] == 0)
 
 
-def test_prologue_composed_full_size_sampled(oracle_lib):
+def _saved_ws(q, v, N):
+    return torch.empty(dn.bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3], v.shape[-1], N),
+                       dtype=torch.uint8, device=DEV)
+
+
+FUSED_CASES = [
+    # B, T, H, Dk, Dv, gated, lengths
+    (2, 150, 2, 128, 128, True, None),
+    (1, 200, 3, 64, 192, False, None),
+    (1, 263, 2, 128, 256, True, (1, 63, 64, 0, 135)),
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED_CASES, ids=lambda c: "B%dT%dH%dk%dv%d-g%d-%s" % (
+    c[:6] + ("packed" if c[6] else "fixed",)))
+def test_bwd_prologue_fused_matches_composed(oracle_lib, cfg):
+    """dn_chunk_bwd_prologue (the prologue's backward folded into the chunk-
+    gradient kernel) against dn_chunk_bwd_saved followed by dn_prologue_bwd:
+    db_in, dx_in, dv, dh0 bit for bit, dq_in and dk_in up to the summation
+    order of the row dot products; zero rows of q_in, k_in give zero gradients;
+    both against the oracle's composition."""
+    B, T, H, Dk, Dv, gated, lens = cfg
+    sh = Shape(B, T, H, Dk, Dv, torch.bfloat16, gated, True, backward=True, lengths=lens)
+    x = make_inputs(sh, seed=90 + T, raw=True)
+    x["q_in"][0, 3, 1] = 0
+    x["k_in"][0, T - 1, 0] = 0
+    d = to_dev(x)
+    c = x["gate_scale"]
+    q, k, beta, g = dn.prologue(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c)
+    ws = _saved_ws(q, d["v"], sh.n_seqs)
+    dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], d["cu_seqlens"], save_workspace=ws)
+    gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"], d["cu_seqlens"], workspace=ws,
+                      saved=True)
+    comp = dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c, gr["dq"], gr["dk"], gr["dbeta"], gr["dg"])
+    fu = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"], d["cu_seqlens"], workspace=ws,
+                      saved=True, prologue_inputs=(d["q_in"], d["k_in"], d["x_in"], c))
+    torch.cuda.synchronize()
+    assert torch.equal(fu["db_in"], comp[2])
+    if gated:
+        assert torch.equal(fu["dx_in"], comp[3])
+    else:
+        assert fu["dx_in"] is None and comp[3] is None
+    assert torch.equal(fu["dv"], gr["dv"]) and torch.equal(fu["dh0"], gr["dh0"])
+    for name, mine, ref in (("dq_in", fu["dq_in"], comp[0]), ("dk_in", fu["dk_in"], comp[1])):
+        e = rel_l2(mine.cpu(), ref.cpu().double().numpy())
+        print(cfg, name, "fused vs composed rel-L2 %.2e" % e, flush=True)
+        assert e < 1e-5, (name, e)
+    assert torch.all(fu["dq_in"].cpu()[0, 3, 1] == 0) and torch.all(fu["dk_in"].cpu()[0, T - 1, 0] == 0)
+    # the oracle's composition
+    rq, rk, rb, rg = oracle_lib.prologue(x["q_in"], x["k_in"], x["b_in"], x["x_in"], c)
+    rgr = oracle_lib.bwd(rq, rk, x["v"], rb, rg, x["h0"], x["dO"], x["dhT"], cu_seqlens=x["cu_seqlens"])
+    rin = oracle_lib.prologue_bwd(x["q_in"], x["k_in"], x["b_in"], x["x_in"], c,
+                                  rgr["dq"], rgr["dk"], rgr["dbeta"], rgr["dg"])
+    for name, r in zip(("dq_in", "dk_in", "db_in", "dx_in"), rin):
+        if r is None:
+            continue
+        e = rel_l2(fu[name].cpu(), r)
+        print(cfg, name, "fused vs oracle rel-L2 %.2e" % e, flush=True)
+        assert e <= TOL, (name, e)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["composed", "fused"])
+def test_prologue_composed_full_size_sampled(oracle_lib, fused):
     """The benchmark's step with the prologue (B=4 T=4096 H=16 dk=128 dv=256):
-    prologue, forward, backward and prologue backward on the GPU against the
+    prologue, forward, backward and prologue backward on the GPU (composed from
+    the separate passes, or with the prologue's backward folded into the
+    chunk-gradient kernel after the state-saving forward pass) against the
     oracle's composition, on two (batch, head) pairs."""
     sh = synth.WORKLOADS[4]
     x = synth.workload_inputs(4, raw=True)
     d = to_dev(x)
     c = x["gate_scale"]
     q, k, beta, g = dn.prologue(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c)
-    o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"])
-    gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"])
-    din = dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c, gr["dq"], gr["dk"],
-                          gr["dbeta"], gr["dg"])
+    if fused:
+        ws = _saved_ws(q, d["v"], sh.n_seqs)
+        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"], save_workspace=ws)
+        gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"], workspace=ws, saved=True,
+                          prologue_inputs=(d["q_in"], d["k_in"], d["x_in"], c))
+        din = [gr["dq_in"], gr["dk_in"], gr["db_in"], gr["dx_in"]]
+    else:
+        o, hT = dn.chunk_fwd(q, k, d["v"], beta, g, d["h0"])
+        gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"])
+        din = dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c, gr["dq"], gr["dk"],
+                              gr["dbeta"], gr["dg"])
     torch.cuda.synchronize()
     o = o.cpu()
     din = [t.cpu() for t in din]

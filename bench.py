@@ -181,14 +181,18 @@ def main():
         if i is not None:
             fev[i][1].record(stream)
         if backward:
-            # nothing is kept between the passes: the backward recomputes eps
-            beta = dn.longhorn_eps(k, b0) if longhorn else b0
+            # the recomputing backward pass keeps nothing from the forward pass and
+            # recomputes eps; the saved-state pair keeps eps beside the states and
+            # folds the step size's backward into the chunk-gradient kernel
+            if not saved:
+                beta = dn.longhorn_eps(k, b0) if longhorn else b0
             fused = saved and args.prologue and not longhorn
             pro = (d["q_in"], d["k_in"], d["x_in"], d["gate_scale"]) if fused else None
             gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"],
                               d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None,
-                              saved=saved, prologue_inputs=pro)
-            if longhorn:
+                              saved=saved, prologue_inputs=pro,
+                              longhorn_beta=b0 if (longhorn and saved) else None)
+            if longhorn and not saved:
                 if i is not None:
                     lev[i][0].record(stream)
                 gr["dbeta"] = dn.longhorn_eps_bwd(k, b0, gr["dbeta"], gr["dk"])
@@ -235,7 +239,7 @@ def main():
                 if j == 0 and saved:
                     continue  # the forward pass stored the states
                 t[name] = us([(bev[i][j], bev[i][j + 1]) for i in idx])
-            if longhorn:
+            if longhorn and not saved:
                 t["longhorn_eps_bwd"] = us([lev[i] for i in idx])
             if args.prologue and not (saved and not longhorn):
                 t["prologue_bwd"] = us([pbev[i] for i in idx])

@@ -78,6 +78,8 @@ def load_library():
     lib.dn_chunk_bwd_prologue.argtypes = ([S] + [P] * 7 + [P, P] + [P, P, P, ctypes.c_float] + [P] * 6
                                           + [P, ctypes.c_size_t, P, P])
     lib.dn_chunk_bwd_prologue.restype = ctypes.c_int
+    lib.dn_chunk_bwd_longhorn.argtypes = [S] + [P] * 7 + [P, P] + [P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
+    lib.dn_chunk_bwd_longhorn.restype = ctypes.c_int
     lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
     lib.dn_recurrent_step.restype = ctypes.c_int
     lib.dn_longhorn_eps.argtypes = [ctypes.c_int32] * 5 + [P] * 3 + [P]
@@ -176,7 +178,7 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_stat
 
 def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 64,
               workspace: Optional[torch.Tensor] = None, events=None, saved: bool = False,
-              prologue_inputs=None):
+              prologue_inputs=None, longhorn_beta: Optional[torch.Tensor] = None):
     """Backward pass of ``<dO, o> + <dhT, hT>``.
 
     Returns a dict of float32 gradients dq, dk, dv, dbeta, dg (None without a
@@ -191,7 +193,10 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     beta, g are ``prologue``'s outputs for these raw inputs, and the dict holds
     the gradients of the raw inputs instead: dq_in, dk_in, db_in, dx_in, with
     dv and dh0 (``dn_chunk_bwd_prologue``: the prologue's backward folded into
-    the chunk-gradient kernel).
+    the chunk-gradient kernel).  ``longhorn_beta`` (with ``saved``): beta is
+    the Longhorn step size ``longhorn_eps(k, longhorn_beta)``; dbeta is then the
+    gradient of ``longhorn_beta`` and dk includes the step size's key term
+    (``dn_chunk_bwd_longhorn``).
     """
     lib = load_library()
     s, N = _shape(q, v, cu_seqlens, chunk)
@@ -226,6 +231,15 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
             if e.cuda_event == 0:  # torch creates the event on its first record
                 e.record(torch.cuda.current_stream(dev))
         ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    if longhorn_beta is not None:
+        if not saved or prologue_inputs is not None:
+            raise ValueError("longhorn_beta needs saved=True and no prologue_inputs")
+        _need(longhorn_beta, "longhorn_beta", torch.float32, (B, T, H), dev)
+        _check("dn_chunk_bwd_longhorn", lib.dn_chunk_bwd_longhorn(
+            ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
+            _ptr(cu_seqlens), _ptr(dO), _ptr(dhT), _ptr(longhorn_beta), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(dbeta), _ptr(dg), _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(dev), ev))
+        return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dh0=dh0)
     if prologue_inputs is not None:
         if not saved:
             raise ValueError("prologue_inputs needs saved=True (the states dn_chunk_fwd_save kept)")

@@ -121,12 +121,13 @@ dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t
   return DN_OK;
 }
 
-// Raw inputs of the input prologue, when its backward is folded into the
-// chunk-gradient kernel.
+// Raw inputs of the input prologue, or the Longhorn step size's beta, when
+// their backward is folded into the chunk-gradient kernel.
 struct ProIn {
   const void *q_in = nullptr, *k_in = nullptr;
   const float *x_in = nullptr;
   float gate_scale = 0.f;
+  const float *beta_raw = nullptr;
 };
 
 // The backward pass.  With `recompute` false it reads the chunk-start states
@@ -193,6 +194,7 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   bp.k_in = pro.k_in;
   bp.x_in = pro.x_in;
   bp.gate_scale = pro.gate_scale;
+  bp.beta_raw = pro.beta_raw;
   return from_hip(dn::launch_bwd(bp, s->dtype, s->Dk, stream, events ? events[2] : nullptr,
                                  events ? events[3] : nullptr));
 }
@@ -305,6 +307,19 @@ dn_status dn_chunk_bwd_prologue(const dn_shape *s, const void *q, const void *k,
   pro.x_in = x_in;
   pro.gate_scale = gate_scale;
   return bwd_run(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq_in, dk_in, dv, db_in, dx_in, dh0, workspace,
+                 workspace_bytes, stream, events, false, pro);
+}
+
+dn_status dn_chunk_bwd_longhorn(const dn_shape *s, const void *q, const void *k, const void *v,
+                                const float *eps, const float *g, const float *h0,
+                                const int32_t *cu_seqlens, const void *dO, const float *dhT,
+                                const float *beta, float *dq, float *dk, float *dv, float *dbeta, float *dg,
+                                float *dh0, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t *events) {
+  if (s && s->T > 0 && !beta) return DN_EINVAL;
+  ProIn pro;
+  pro.beta_raw = beta ? beta : eps;  // T == 0: nothing is read, but the variant is still the folded one
+  return bwd_run(s, q, k, v, eps, g, h0, cu_seqlens, dO, dhT, dq, dk, dv, dbeta, dg, dh0, workspace,
                  workspace_bytes, stream, events, false, pro);
 }
 

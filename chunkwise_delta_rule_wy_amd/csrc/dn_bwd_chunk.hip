@@ -112,10 +112,17 @@ struct BwdKsw {
 };
 
 
-// PRO: the input prologue's backward is folded into the stores (the gradients
-// of q_in, k_in, b_in, x_in replace those of q, k, beta, g).
-template <int DK, bool GATED, bool PRO>
+// Epilogues of the chunk-gradient kernel: the plain gradients; EPI_PRO folds
+// the input prologue's backward into the stores (the gradients of q_in, k_in,
+// b_in, x_in replace those of q, k, beta, g); EPI_LH folds in the Longhorn
+// step size (beta holds eps = beta_raw / (1 + beta_raw |k|^2): dbeta becomes
+// the gradient of beta_raw, deps (eps / beta_raw)^2, and dk gains
+// -2 eps^2 deps k, the step size's dependence on the key).
+enum : int { EPI_PLAIN = 0, EPI_PRO = 1, EPI_LH = 2 };
+
+template <int DK, bool GATED, int EPI>
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
+  constexpr bool PRO = EPI == EPI_PRO, LH = EPI == EPI_LH;
   using LY = BLay<DK>;
   using RS = Res<MODE_CHUNK>;
   constexpr int KB = LY::KB, MT = LY::MT, RB = LY::RB;
@@ -497,6 +504,14 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           const float bt = ld<float>(sb + LY::O_BETA + 4 * r);
           p.dbeta[idx] = dbeta * bt * (1.f - bt);
           if (GATED) p.dg[idx] = -p.gate_scale * dgr / (1.f + expf(-p.x_in[idx]));
+        } else if constexpr (LH) {
+          // dbeta_raw = deps / (1 + beta_raw |k|^2)^2 = deps (eps / beta_raw)^2 (deps at beta_raw = 0);
+          // deps goes to the row waves for the key term
+          const float br = p.beta_raw[idx], ep = ld<float>(sb + LY::O_BETA + 4 * r);
+          const float ratio = br != 0.f ? ep / br : 1.f;
+          p.dbeta[idx] = dbeta * ratio * ratio;
+          st<float>(red + 3072 + 4 * r, dbeta);
+          if (GATED) p.dg[idx] = dgr;
         } else {
           p.dbeta[idx] = dbeta;
           if (GATED) p.dg[idx] = dgr;
@@ -710,7 +725,20 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     }
     mfma_settle();
     __syncthreads();  // the column part of dk is in LDS
-    if constexpr (PRO) {
+    if constexpr (LH) {
+      // dk += -2 eps^2 deps k (row rr; k from the chunk's K tile, columns 16mt + 4g ..)
+      const float ep = ld<float>(sb + LY::O_BETA + 4 * rr);
+      const float c = -2.f * ep * ep * (rr < L ? ld<float>(red + 3072 + 4 * rr) : 0.f);
+      const int sk = swz_s<DK>(n);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x4 kv = ld<bf16x4>(sb + LY::O_K + rr * RB + 8 * (g & 1) + 16 * ((2 * mt + (g >> 1)) ^ sk));
+        f32x4 dk = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dk[e] += c * bf2f(kv[e]);
+        if (rr < L) *reinterpret_cast<f32x4 *>(dkb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dk;
+      }
+    } else if constexpr (PRO) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) dkr[mt] = dkr[mt] + ld<f32x4>(dkx + 16 * ((rho * MT + mt) * 64 + l));
       pro_norm(dkr, xk);
@@ -731,8 +759,9 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 template <int DK>
 hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   const size_t smem = BLay<DK>::TOTAL;
-  auto kern = p.q_in ? (p.g ? bwd_chunk_kernel<DK, true, true> : bwd_chunk_kernel<DK, false, true>)
-                     : (p.g ? bwd_chunk_kernel<DK, true, false> : bwd_chunk_kernel<DK, false, false>);
+  auto kern = p.q_in       ? (p.g ? bwd_chunk_kernel<DK, true, EPI_PRO> : bwd_chunk_kernel<DK, false, EPI_PRO>)
+              : p.beta_raw ? (p.g ? bwd_chunk_kernel<DK, true, EPI_LH> : bwd_chunk_kernel<DK, false, EPI_LH>)
+                           : (p.g ? bwd_chunk_kernel<DK, true, EPI_PLAIN> : bwd_chunk_kernel<DK, false, EPI_PLAIN>);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;

@@ -39,6 +39,10 @@ struct BwdParams {
   const void *q_in, *k_in;
   const float *x_in;
   float gate_scale;
+  // Longhorn step size folded in (beta_raw set): beta holds eps = beta_raw /
+  // (1 + beta_raw |k|^2), dbeta receives the gradient of beta_raw and dk the
+  // step size's key term
+  const float *beta_raw;
 };
 
 struct StepParams {

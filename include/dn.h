@@ -196,6 +196,29 @@ dn_status dn_chunk_bwd_prologue(const dn_shape *s,
                                 hipEvent_t *events);
 
 /*
+ * dn_chunk_bwd_saved for the Longhorn recurrence, with the step size's
+ * backward folded in: the recurrence ran at beta := eps = beta / (1 + beta
+ * |k|^2) (dn_longhorn_eps; Gated DeltaNet review thread, Table 1, row
+ * "Longhorn"), `eps` is that step size and `beta` the raw one.  Writes dq,
+ * dv, dg, dh0 as dn_chunk_bwd_saved, dk with the step size's key term
+ * -2 eps^2 deps k added, and dbeta, the gradient of the raw beta,
+ * deps / (1 + beta |k|^2)^2.  The same values as dn_chunk_bwd_saved followed
+ * by dn_longhorn_eps_bwd up to rounding (here (eps / beta)^2 stands for
+ * 1 / (1 + beta |k|^2)^2).  The workspace is the one dn_chunk_fwd_save filled
+ * with beta := eps.  Errors as dn_chunk_bwd_saved, and DN_EINVAL for a null
+ * beta (T > 0).
+ */
+dn_status dn_chunk_bwd_longhorn(const dn_shape *s,
+                                const void *q, const void *k, const void *v,
+                                const float *eps, const float *g, const float *h0,
+                                const int32_t *cu_seqlens,
+                                const void *dO, const float *dhT,
+                                const float *beta,
+                                float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t *events);
+
+/*
  * One recurrent (decode) step for B x H independent states: the token update
  * above applied once (Gated DeltaNet review thread, General Response 2: the
  * recurrent step is memory-bound and its cost is set by the state size).

@@ -238,3 +238,19 @@ def test_bwd_prologue_validation(lib):
     need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
     assert call(wsb=need - 1) == DN_ENOWS
     assert call(dtype_shape=shape(dtype=0)) == DN_EUNSUPPORTED
+
+
+def test_bwd_longhorn_validation(lib):
+    P = ctypes.c_void_p
+    s = shape()
+    f = lib.dn_chunk_bwd_longhorn
+    f.argtypes = [ctypes.c_void_p] + [P] * 7 + [P, P] + [P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
+
+    def call(beta=FAKE, g=None, dg=None, wsb=1 << 40, sh=s):
+        return f(ctypes.byref(sh), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(g), None, None, P(FAKE), None,
+                 P(beta), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(dg), None, P(FAKE), wsb, None, None)
+    assert call(beta=None) == DN_EINVAL
+    assert call(g=FAKE, dg=None) == DN_EINVAL
+    need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
+    assert call(wsb=need - 1) == DN_ENOWS
+    assert call(sh=shape(dtype=0)) == DN_EUNSUPPORTED

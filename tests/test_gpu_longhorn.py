@@ -149,3 +149,51 @@ def test_longhorn_full_size_sampled(oracle_lib):
               flush=True)
         for name, e in errs.items():
             assert e <= TOL, (name, e)
+
+
+FOLDED_CASES = [
+    # B, T, H, Dk, Dv, gated, h0, lengths
+    (2, 150, 2, 128, 128, True, True, None),
+    (1, 200, 3, 64, 192, False, False, None),
+    (1, 263, 2, 128, 256, True, True, (1, 63, 64, 0, 135)),
+]
+
+
+@pytest.mark.parametrize("cfg", FOLDED_CASES, ids=lambda c: "B%dT%dH%dk%dv%d-g%d-h%d-%s" % (
+    c[:7] + ("packed" if c[7] else "fixed",)))
+def test_longhorn_folded_backward(oracle_lib, cfg):
+    """dn_chunk_bwd_longhorn (the step size's backward folded into the chunk-
+    gradient kernel, after the state-saving forward pass at beta := eps)
+    against dn_chunk_bwd_saved followed by dn_longhorn_eps_bwd: dq, dv, dg,
+    dh0 bit for bit, dk and dbeta up to rounding; and against the oracle."""
+    B, T, H, Dk, Dv, gated, h0, lens = cfg
+    sh = Shape(B, T, H, Dk, Dv, torch.bfloat16, gated, h0, backward=True, lengths=lens)
+    x = scale_keys(make_inputs(sh, seed=60 + T), seed=61)
+    x["beta"][0, 2, 0] = 0.0  # a zero step
+    d = to_dev(x)
+    eps = dn.longhorn_eps(d["k"], d["beta"])
+    ws = torch.empty(dn.bwd_workspace_bytes(B, T, H, Dk, Dv, sh.n_seqs), dtype=torch.uint8, device=DEV)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], eps, d["g"], d["h0"], d["cu_seqlens"], save_workspace=ws)
+    gr = dn.chunk_bwd(d["q"], d["k"], d["v"], eps, d["g"], d["h0"], d["dO"], d["dhT"], d["cu_seqlens"],
+                      workspace=ws, saved=True)
+    comp_db = dn.longhorn_eps_bwd(d["k"], d["beta"], gr["dbeta"], gr["dk"])
+    fo = dn.chunk_bwd(d["q"], d["k"], d["v"], eps, d["g"], d["h0"], d["dO"], d["dhT"], d["cu_seqlens"],
+                      workspace=ws, saved=True, longhorn_beta=d["beta"])
+    torch.cuda.synchronize()
+    for name in ("dq", "dv", "dg", "dh0"):
+        if gr[name] is None:
+            assert fo[name] is None
+        else:
+            assert torch.equal(fo[name], gr[name]), name
+    for name, mine, ref in (("dk", fo["dk"], gr["dk"]), ("dbeta", fo["dbeta"], comp_db)):
+        e = rel_l2(mine.cpu(), ref.cpu().double().numpy())
+        print(cfg, name, "folded vs composed rel-L2 %.2e" % e, flush=True)
+        assert e < 1e-5, (name, e)
+    ref = oracle_lib.longhorn_bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["dO"], x["dhT"],
+                                  cu_seqlens=x["cu_seqlens"])
+    for name in NAMES:
+        if ref[name] is None:
+            continue
+        e = rel_l2(fo[name].cpu(), ref[name])
+        print(cfg, name, "folded vs oracle rel-L2 %.2e" % e, flush=True)
+        assert e <= TOL, (name, e)

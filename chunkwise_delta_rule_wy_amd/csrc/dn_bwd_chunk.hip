@@ -656,7 +656,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     // loaded here, ahead of use; dq and dk stay in registers until |q_in|^2 and
     // q_in . dq are summed over the row's four lanes.  Rows past the chunk read
     // the chunk's first row (their results are not stored).
-    bf16x4 xq[PRO ? MT : 1], xk[PRO ? MT : 1];
+    bf16x4 xq[MT], xk[MT];  // unused (and removed by the compiler) without PRO
     if constexpr (PRO) {
       const size_t xrow = ((row0 + (rr < L ? rr : 0)) * H + h) * (size_t)DK + 4 * g;
 #pragma unroll
@@ -666,13 +666,13 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       }
     }
     // (d - x (x . d) / |x|^2) / |x| over the row, in place
-    auto pro_norm = [&](f32x4 (&d)[MT], const bf16x4 (&x)[PRO ? MT : 1]) {
+    auto pro_norm = [&](f32x4 (&d)[MT], const bf16x4 (&x)[MT]) {
       float sq = 0.f, pd = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float xv = bf2f(x[mt < (PRO ? MT : 1) ? mt : 0][e]);
+          const float xv = bf2f(x[mt][e]);
           sq += xv * xv;
           pd += xv * d[mt][e];
         }
@@ -682,12 +682,12 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[mt][e] = (d[mt][e] - bf2f(x[mt < (PRO ? MT : 1) ? mt : 0][e]) * c) * inv;
+        for (int e = 0; e < 4; ++e) d[mt][e] = (d[mt][e] - bf2f(x[mt][e]) * c) * inv;
     };
     // dq = diag(gamma) dO h^T + dPG K ;  dk (row part) = diag(w) V' dh^T - diag(gamma beta) Y h^T + F K,
     // as dq^T = gamma dq1^T + K^T dPG^T (and likewise dk): lane (n, g) holds row r = 16rho + n,
     // columns 16mt + 4g .. + 3, written as one 16-byte store
-    f32x4 dkr[MT], dqv[PRO ? MT : 1];
+    f32x4 dkr[MT], dqv[MT];  // dqv: PRO only
     {
       bf16x8 pgr[2], fr[2];  // B operands: rows r of dPG and F, read transposed from dPG^T, F^T
 #pragma unroll

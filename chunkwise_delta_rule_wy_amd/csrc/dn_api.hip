@@ -106,7 +106,8 @@ dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t
   const bool varlen = cu != nullptr;
   // the workspace query cannot see cu_seqlens, so it sizes for the varlen bound
   const BwdLayout L = bwd_layout(s, varlen || s->B == 1);
-  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return DN_ENOWS;
+  // a shape that needs no workspace (no chunk at all) accepts a null one
+  if (workspace_bytes < L.total || (L.total > 0 && (!workspace || !aligned16(workspace)))) return DN_ENOWS;
   char *ws = static_cast<char *>(workspace);
   w.nchunks = max_chunks(s, varlen);
   w.chunk_base = w.chunk_seq = nullptr;

@@ -254,3 +254,15 @@ def test_bwd_longhorn_validation(lib):
     need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
     assert call(wsb=need - 1) == DN_ENOWS
     assert call(sh=shape(dtype=0)) == DN_EUNSUPPORTED
+
+
+def test_empty_shape_needs_no_workspace(lib):
+    # T = 0 with B > 1: no chunk, so the backward workspace is empty and may be null;
+    # the call then enqueues only the pass-through of dhT to dh0 (not run here:
+    # validation is all this checks, with an output pointer left null on purpose)
+    s = shape(T=0)
+    assert lib.dn_chunk_bwd_workspace(ctypes.byref(s)) == 0
+    P = ctypes.c_void_p
+    st = lib.dn_chunk_fwd_save(ctypes.byref(shape(T=0, dtype=0)), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None,
+                               None, P(FAKE), None, None, 0, None)
+    assert st == DN_EUNSUPPORTED  # dtype is checked before the workspace

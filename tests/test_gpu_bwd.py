@@ -257,3 +257,17 @@ def test_strong_decay_parity(oracle_lib, saved):
     print("strong decay forward rel-L2 o %.2e hT %.2e" % (eo, eh), flush=True)
     assert eo <= TOL and eh <= TOL
     check_bwd(x, oracle_lib, "strong decay", saved)
+
+
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_varlen_all_empty(saved):
+    """Packed input whose sequences are all empty (T = 0, three sequences):
+    hT = h0 and dh0 = dhT per sequence."""
+    sh = Shape(1, 0, 2, 128, 128, torch.bfloat16, True, True, backward=True, lengths=(0, 0, 0))
+    x = make_inputs(sh, seed=9)
+    d = to_dev(x)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(hT.cpu(), x["h0"])
+    gr = gpu_bwd(x, saved)
+    assert torch.equal(gr["dh0"], x["dhT"])

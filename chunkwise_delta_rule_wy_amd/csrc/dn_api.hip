@@ -104,12 +104,14 @@ struct TrainWs {
 dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t workspace_bytes,
                    hipStream_t stream, TrainWs &w) {
   const bool varlen = cu != nullptr;
+  w.nchunks = max_chunks(s, varlen);
+  // the chunk-parallel kernel launches one workgroup per (chunk, head)
+  if (w.nchunks * s->H >= (int64_t)INT32_MAX) return DN_EUNSUPPORTED;
   // the workspace query cannot see cu_seqlens, so it sizes for the varlen bound
   const BwdLayout L = bwd_layout(s, varlen || s->B == 1);
   // a shape that needs no workspace (no chunk at all) accepts a null one
   if (workspace_bytes < L.total || (L.total > 0 && (!workspace || !aligned16(workspace)))) return DN_ENOWS;
   char *ws = static_cast<char *>(workspace);
-  w.nchunks = max_chunks(s, varlen);
   w.chunk_base = w.chunk_seq = nullptr;
   if (varlen) {
     w.chunk_base = reinterpret_cast<int32_t *>(ws + L.table);

@@ -39,8 +39,9 @@
  *   chunk == 64 (dn_chunk_fwd also takes chunk == 32 for DN_BF16 inputs: the
  *   same result with 32-token chunks); dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
  *   pointers 16-byte aligned; 256 H max(Dk, Dv) < 2^31 (the byte span of one
- *   64-token chunk of fp32 rows, addressed with 32-bit offsets).  Shapes
- *   outside these limits return DN_EUNSUPPORTED.
+ *   64-token chunk of fp32 rows, addressed with 32-bit offsets); for the
+ *   backward passes, fewer than 2^31 (chunk, head) pairs.  Shapes outside
+ *   these limits return DN_EUNSUPPORTED.
  */
 #ifndef DN_H_
 #define DN_H_

@@ -266,3 +266,10 @@ def test_empty_shape_needs_no_workspace(lib):
     st = lib.dn_chunk_fwd_save(ctypes.byref(shape(T=0, dtype=0)), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None,
                                None, P(FAKE), None, None, 0, None)
     assert st == DN_EUNSUPPORTED  # dtype is checked before the workspace
+
+
+def test_bwd_rejects_too_many_chunk_head_pairs(lib):
+    # 2^24 chunks x 8192 heads exceeds the chunk-parallel kernel's grid
+    s = shape(B=1, T=1 << 30, H=8192, n_seqs=1)
+    assert bwd(lib, s) == DN_EUNSUPPORTED
+    assert fwd_save(lib, s) == DN_EUNSUPPORTED

@@ -124,6 +124,18 @@ def _need(t, name, dtype, shape, dev):
     return t
 
 
+def _workspace(ws, dev, nbytes, name):
+    """Check a caller's workspace: a contiguous uint8 tensor on the inputs'
+    device holding at least nbytes."""
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise TypeError("%s must be a contiguous uint8 tensor" % name)
+    if ws.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, ws.device, dev))
+    if ws.numel() < nbytes:
+        raise ValueError("%s holds %d bytes, %d needed" % (name, ws.numel(), nbytes))
+    return ws
+
+
 def _shape(q, v, cu_seqlens, chunk):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, Dk]")
@@ -163,6 +175,7 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, cu_seqlens=None, output_final_stat
     o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
     hT = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
     if save_workspace is not None:
+        _workspace(save_workspace, dev, lib.dn_chunk_bwd_workspace(ctypes.byref(s)), "save_workspace")
         _check("dn_chunk_fwd_save", lib.dn_chunk_fwd_save(
             ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0),
             _ptr(cu_seqlens), _ptr(o), _ptr(hT), _ptr(save_workspace), save_workspace.numel(),
@@ -221,8 +234,10 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     wsb = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
     if saved and workspace is None:
         raise ValueError("saved=True needs the workspace that chunk_fwd filled")
-    if workspace is None or workspace.numel() < wsb:
+    if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    else:
+        _workspace(workspace, dev, wsb, "workspace")
     ev = None
     if events is not None:
         if len(events) != 4:

@@ -273,3 +273,18 @@ def test_bwd_rejects_too_many_chunk_head_pairs(lib):
     s = shape(B=1, T=1 << 30, H=8192, n_seqs=1)
     assert bwd(lib, s) == DN_EUNSUPPORTED
     assert fwd_save(lib, s) == DN_EUNSUPPORTED
+
+
+def test_binding_checks_caller_workspaces():
+    import torch
+    cpu = torch.device("cpu")
+    ok = torch.empty(64, dtype=torch.uint8)
+    assert dn._workspace(ok, cpu, 64, "ws") is ok
+    with pytest.raises(ValueError):
+        dn._workspace(ok, cpu, 65, "ws")  # too small: never silently replaced
+    with pytest.raises(TypeError):
+        dn._workspace(torch.empty(16, dtype=torch.float32), cpu, 8, "ws")
+    with pytest.raises(TypeError):
+        dn._workspace(torch.empty(64, dtype=torch.uint8)[::2], cpu, 8, "ws")
+    with pytest.raises(ValueError):
+        dn._workspace(ok, torch.device("cuda:0"), 8, "ws")  # on another device than the inputs

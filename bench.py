@@ -37,6 +37,64 @@ CHUNK_GRAD_TRAFFIC_W4 = 1511.6e6
 # H=16 dk=128 dv=256): 294.0 MB read + 142.6 MB written
 FWD_TRAFFIC_W3 = 436.6e6
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
+PROBE_LIB = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
+_probe = None
+
+
+def probe_lib():
+    """libdnprobe.so (built beside libdn.so): machine probes and timing events."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError("%s is not built: run __graft_entry__.build()" % PROBE_LIB)
+        lib = ctypes.CDLL(PROBE_LIB)
+        vp = ctypes.c_void_p
+        lib.dnp_event_create.argtypes = [ctypes.POINTER(vp)]
+        lib.dnp_event_destroy.argtypes = [vp]
+        lib.dnp_event_record.argtypes = [vp, vp]
+        lib.dnp_event_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
+        lib.dnp_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+        lib.dnp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.dnp_mfma_loop_flops.restype = ctypes.c_double
+        lib.dnp_clock.argtypes = [ctypes.c_ulonglong, vp, vp]
+        lib.dnp_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+        _probe = lib
+    return _probe
+
+
+class TimingEvent:
+    """A HIP event made for timing only: recording it takes a timestamp after
+    the work enqueued before it on the stream, without the system-scope cache
+    write-back and invalidation of a default event (torch.cuda.Event), which
+    costs the kernels that follow it several microseconds per record.  The
+    binding takes it wherever it takes a torch.cuda.Event (`cuda_event`)."""
+
+    def __init__(self):
+        import ctypes
+        h = ctypes.c_void_p()
+        if probe_lib().dnp_event_create(ctypes.byref(h)) != 0:
+            raise RuntimeError("dnp_event_create failed")
+        self.cuda_event = h.value
+
+    def record(self, stream):
+        import ctypes
+        if probe_lib().dnp_event_record(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("dnp_event_record failed")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (waits for `end`)."""
+        import ctypes
+        ms = ctypes.c_float()
+        if probe_lib().dnp_event_elapsed_ms(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(end.cuda_event),
+                                            ctypes.byref(ms)) != 0:
+            raise RuntimeError("dnp_event_elapsed_ms failed")
+        return ms.value
+
+    def __del__(self):
+        import ctypes
+        if _probe is not None and self.cuda_event:
+            _probe.dnp_event_destroy(ctypes.c_void_p(self.cuda_event))
 
 
 def workload_bytes(sh, backward: bool) -> float:
@@ -91,8 +149,9 @@ def fwd_flops(sh) -> float:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the clocks take some 40 steps of steady work to settle after a start
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default="4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -149,7 +208,7 @@ def main():
     # every timed step records HIP events on the stream the kernels run on
     # (torch's current stream, which the binding hands to the library)
     stream = torch.cuda.current_stream(dev)
-    mk = lambda: torch.cuda.Event(enable_timing=True)
+    mk = TimingEvent
     nev = max(args.steps, 1) + max(args.cold_steps, 0)
     fev = [(mk(), mk()) for _ in range(nev)]
     bev = [[mk() for _ in range(4)] for _ in range(nev)] if backward else None
@@ -308,7 +367,6 @@ def main():
         e0.record(stream)
         b.copy_(a)
         e1.record(stream)
-        e1.synchronize()
         out["copy_512MiB_us"] = round(e0.elapsed_time(e1) * 1e3, 1)
         del a, b
     if not args.no_cpu_baseline:
@@ -322,29 +380,18 @@ def measured_peaks(torch, dev, stream):
     plain MFMA loop (16x16x32 MFMAs on registers, four waves per SIMD) and the
     shader clock (a wave spinning on the clock counter, against HIP events)."""
     import ctypes
-    path = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
-    if not os.path.exists(path):
-        print("measured peaks skipped: %s is not built" % path, file=sys.stderr)
-        return None
-    lib = ctypes.CDLL(path)
-    lib.dnp_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.dnp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
-    lib.dnp_mfma_loop_flops.restype = ctypes.c_double
-    lib.dnp_clock.argtypes = [ctypes.c_ulonglong, ctypes.c_void_p, ctypes.c_void_p]
+    lib = probe_lib()
     sp = ctypes.c_void_p(stream.cuda_stream)
-    ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def timed(fn, reps):
         fn()
-        e0, e1 = ev(), ev()
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for _ in range(reps):
             fn()
         e1.record(stream)
-        e1.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / reps
 
-    lib.dnp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     a = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
     t_torch = timed(lambda: b.copy_(a), 5)
@@ -446,14 +493,12 @@ def bench_decode(args, dn, synth, dev):
     for _ in range(args.warmup):
         dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], st)
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = TimingEvent(), TimingEvent()
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
         dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], st)
     ev1.record(stream)
-    ev1.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / args.steps
     B, H, Dk, Dv = 256, 32, 128, 128
     nbytes = B * H * Dk * Dv * 4 * 2 + B * H * (2 * Dk + 2 * Dv) * 2 + B * H * 8

@@ -2,7 +2,8 @@
 // streaming copy reaches, the bf16 matrix-core rate a plain MFMA loop reaches,
 // and the shader clock.  Built into its own library
 // (libdnprobe.so), apart from the operation's library; bench.py times the
-// launches with HIP events on the stream it passes.
+// launches with HIP events on the stream it passes, and takes its timing
+// events from here too.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -105,6 +106,28 @@ int dnp_clock(unsigned long long cycles, unsigned long long *out, hipStream_t st
   if (cycles == 0 || cycles > (1ull << 32) || !out) return -1;
   hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, stream, cycles, out);
   return (int)hipGetLastError();
+}
+
+// Timing events for the benchmark: created with hipEventDisableSystemFence,
+// so that recording one does not write back and invalidate the caches at
+// system scope (the default event does, which slows the kernels that follow).
+// Their timestamps still mark the end of the work enqueued before them on
+// the stream.  Each call returns 0 or the HIP error code.
+int dnp_event_create(hipEvent_t *ev) {
+  if (!ev) return -1;
+  return (int)hipEventCreateWithFlags(ev, hipEventDisableSystemFence);
+}
+
+int dnp_event_destroy(hipEvent_t ev) { return (int)hipEventDestroy(ev); }
+
+int dnp_event_record(hipEvent_t ev, hipStream_t stream) { return (int)hipEventRecord(ev, stream); }
+
+// Milliseconds between two recorded events; waits for `end` to complete.
+int dnp_event_elapsed_ms(hipEvent_t start, hipEvent_t end, float *ms) {
+  if (!ms) return -1;
+  const hipError_t e = hipEventSynchronize(end);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipEventElapsedTime(ms, start, end);
 }
 
 }  // extern "C"

@@ -202,8 +202,13 @@ def test_probe_library_exports_and_validates():
     # the benchmark's machine probes: own library, host-side argument checks
     path = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
     plib = ctypes.CDLL(path)
-    for name in ("dnp_mfma_loop", "dnp_mfma_loop_flops", "dnp_clock", "dnp_copy"):
+    for name in ("dnp_mfma_loop", "dnp_mfma_loop_flops", "dnp_clock", "dnp_copy", "dnp_event_create",
+                 "dnp_event_destroy", "dnp_event_record", "dnp_event_elapsed_ms"):
         assert hasattr(plib, name), name
+    plib.dnp_event_create.argtypes = [ctypes.c_void_p]
+    assert plib.dnp_event_create(None) == -1
+    plib.dnp_event_elapsed_ms.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert plib.dnp_event_elapsed_ms(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == -1
     plib.dnp_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     plib.dnp_mfma_loop_flops.restype = ctypes.c_double
     assert plib.dnp_mfma_loop_flops(2, 3) == 2 * 4 * 3 * 16 * 16384

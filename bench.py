@@ -19,6 +19,7 @@ throughput on a bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -45,7 +46,6 @@ def probe_lib():
     """libdnprobe.so (built beside libdn.so): machine probes and timing events."""
     global _probe
     if _probe is None:
-        import ctypes
         if not os.path.exists(PROBE_LIB):
             raise RuntimeError("%s is not built: run __graft_entry__.build()" % PROBE_LIB)
         lib = ctypes.CDLL(PROBE_LIB)
@@ -71,20 +71,17 @@ class TimingEvent:
     binding takes it wherever it takes a torch.cuda.Event (`cuda_event`)."""
 
     def __init__(self):
-        import ctypes
         h = ctypes.c_void_p()
         if probe_lib().dnp_event_create(ctypes.byref(h)) != 0:
             raise RuntimeError("dnp_event_create failed")
         self.cuda_event = h.value
 
     def record(self, stream):
-        import ctypes
         if probe_lib().dnp_event_record(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream.cuda_stream)) != 0:
             raise RuntimeError("dnp_event_record failed")
 
     def elapsed_time(self, end) -> float:
         """Milliseconds from this event to `end` (waits for `end`)."""
-        import ctypes
         ms = ctypes.c_float()
         if probe_lib().dnp_event_elapsed_ms(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(end.cuda_event),
                                             ctypes.byref(ms)) != 0:
@@ -92,9 +89,9 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        import ctypes
         if _probe is not None and self.cuda_event:
             _probe.dnp_event_destroy(ctypes.c_void_p(self.cuda_event))
+            self.cuda_event = None
 
 
 def workload_bytes(sh, backward: bool) -> float:
@@ -379,7 +376,6 @@ def measured_peaks(torch, dev, stream):
     a 1 GiB device copy (bytes read + written over time), the bf16 rate of a
     plain MFMA loop (16x16x32 MFMAs on registers, four waves per SIMD) and the
     shader clock (a wave spinning on the clock counter, against HIP events)."""
-    import ctypes
     lib = probe_lib()
     sp = ctypes.c_void_p(stream.cuda_stream)
 

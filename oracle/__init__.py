@@ -10,7 +10,8 @@ its sequential adjoint, and a single recurrent step; and the Longhorn row of
 the same table (the delta rule at the step size beta / (1 + beta |k|^2)),
 with its gradient by the chain rule through that step size; and the input
 prologue of the workloads (L2-normalised q and k, sigmoid beta, negative
-softplus log-gate) with its gradient, in numpy float64.
+softplus log-gate) with its gradient, and the depthwise causal short
+convolution with its adjoint, in numpy float64.
 
 Inputs may be torch tensors (any float dtype, on any device) or numpy arrays;
 they are upcast exactly to float64 on the host.  Results are float64 numpy.
@@ -221,3 +222,55 @@ def prologue_bwd(q_in, k_in, b_in, g_in, gate_scale, dq, dk, dbeta, dg=None):
     if g_in is not None:
         dg_in = -float(gate_scale) * dg / (1.0 + np.exp(-g_in))
     return unit_bwd(q_in, dq), unit_bwd(k_in, dk), db_in, dg_in
+
+
+# ------------------------------------------------------------- short convolution
+# The depthwise "short convolution" that the DeltaNet rebuttal (answer W2)
+# names beside the token mixer: every channel of every head is filtered along
+# time by its own W taps, causally, so a token sees itself and the W - 1
+# tokens before it in its own sequence (zeros before the sequence start).
+# The pages give neither the width nor an activation; the width is the
+# caller's and no activation is applied.
+
+def _seq_ranges(B, T, cu_seqlens):
+    """(batch row, first token, end token) of every sequence."""
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(c) for c in _i32(cu_seqlens)]
+    return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def short_conv(x, w, cu_seqlens=None):
+    """y[t, h, c] = sum_{j < W} w[h, c, j] x[t - (W - 1) + j, h, c] inside each
+    sequence (tap W - 1 is the current token).  x [B, T, H, D] (packed: B = 1
+    with cu_seqlens [N + 1]), w [H, D, W].  Returns y in float64."""
+    x, w = _f64(x), _f64(w)
+    B, T = x.shape[:2]
+    W = w.shape[-1]
+    y = np.zeros_like(x)
+    for b, t0, t1 in _seq_ranges(B, T, cu_seqlens):
+        L = t1 - t0
+        for j in range(W):
+            s = W - 1 - j  # tap j reads the token s steps back
+            if s < L:
+                y[b, t0 + s:t1] += w[:, :, j] * x[b, t0:t1 - s]
+    return y
+
+
+def short_conv_bwd(x, w, dy, cu_seqlens=None):
+    """Adjoint of short_conv: dx[t] = sum_j w[j] dy[t + (W - 1) - j] over the
+    outputs of the same sequence, dw[h, c, j] = sum_t dy[t] x[t - (W - 1) + j].
+    Returns (dx, dw) in float64."""
+    x, w, dy = _f64(x), _f64(w), _f64(dy)
+    B, T = x.shape[:2]
+    W = w.shape[-1]
+    dx = np.zeros_like(x)
+    dw = np.zeros_like(w)
+    for b, t0, t1 in _seq_ranges(B, T, cu_seqlens):
+        L = t1 - t0
+        for j in range(W):
+            s = W - 1 - j
+            if s < L:
+                dx[b, t0:t1 - s] += w[:, :, j] * dy[b, t0 + s:t1]
+                dw[:, :, j] += np.sum(dy[b, t0 + s:t1] * x[b, t0:t1 - s], axis=0)
+    return dx, dw

@@ -90,6 +90,10 @@ def load_library():
     lib.dn_prologue.restype = ctypes.c_int
     lib.dn_prologue_bwd.argtypes = [ctypes.c_int32] * 5 + [P] * 4 + [ctypes.c_float] + [P] * 8 + [P]
     lib.dn_prologue_bwd.restype = ctypes.c_int
+    lib.dn_short_conv.argtypes = [ctypes.c_int32] * 7 + [P] * 4 + [P]
+    lib.dn_short_conv.restype = ctypes.c_int
+    lib.dn_short_conv_bwd.argtypes = [ctypes.c_int32] * 7 + [P] * 6 + [P]
+    lib.dn_short_conv_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -402,6 +406,51 @@ def prologue_bwd(q_in, k_in, b_in, x_in, gate_scale, dq, dk, dbeta, dg=None):
         float(gate_scale), _ptr(dq), _ptr(dk), _ptr(dbeta), _ptr(dg), _ptr(dq_in), _ptr(dk_in),
         _ptr(db_in), _ptr(dx_in), _stream(dev)))
     return dq_in, dk_in, db_in, dx_in
+
+
+def _conv_dims(x, w, cu_seqlens):
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a [B, T, H, D] tensor")
+    if x.dtype not in _DTYPES:
+        raise TypeError("x must be float32 or bfloat16")
+    B, T, H, D = x.shape
+    if not isinstance(w, torch.Tensor) or w.dim() != 3 or tuple(w.shape[:2]) != (H, D):
+        raise ValueError("w must be a [H, D, W] tensor")
+    W = w.shape[2]
+    _need(w, "w", torch.float32, (H, D, W), x.device)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    n_seqs = B
+    if cu_seqlens is not None:
+        n_seqs = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (n_seqs + 1,), x.device)
+    return B, T, H, D, W, n_seqs
+
+
+def short_conv(x, w, cu_seqlens=None):
+    """Depthwise causal short convolution (``dn_short_conv``): y[t] = sum_j
+    w[:, :, j] x[t - (W - 1) + j] inside each sequence; x [B, T, H, D], w
+    [H, D, W] float32.  Returns y (dtype of x)."""
+    lib = load_library()
+    B, T, H, D, W, n = _conv_dims(x, w, cu_seqlens)
+    y = torch.empty_like(x)
+    _check("dn_short_conv", lib.dn_short_conv(
+        B, T, H, D, W, n, _DTYPES[x.dtype], _ptr(x), _ptr(w), _ptr(cu_seqlens), _ptr(y), _stream(x.device)))
+    return y
+
+
+def short_conv_bwd(x, w, dy, cu_seqlens=None):
+    """Backward of ``short_conv`` (``dn_short_conv_bwd``): float32 (dx, dw)
+    from dy = dL/dy (float32, the shape of x)."""
+    lib = load_library()
+    B, T, H, D, W, n = _conv_dims(x, w, cu_seqlens)
+    _need(dy, "dy", torch.float32, tuple(x.shape), x.device)
+    dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    dw = torch.empty(w.shape, dtype=torch.float32, device=x.device)
+    _check("dn_short_conv_bwd", lib.dn_short_conv_bwd(
+        B, T, H, D, W, n, _DTYPES[x.dtype], _ptr(x), _ptr(w), _ptr(cu_seqlens), _ptr(dy), _ptr(dx),
+        _ptr(dw), _stream(x.device)))
+    return dx, dw
 
 
 class DeltaRule(torch.autograd.Function):

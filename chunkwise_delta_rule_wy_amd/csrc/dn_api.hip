@@ -445,4 +445,57 @@ dn_status dn_prologue_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t d
   return from_hip(dn::launch_prologue(p, dtype, Dk, true, stream));
 }
 
+static dn_status conv_check(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                            int32_t dtype, const int32_t *cu_seqlens) {
+  if (B <= 0 || T < 0 || H <= 0 || D <= 0) return DN_EINVAL;
+  if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+  if (cu_seqlens ? (B != 1 || n_seqs < 1) : n_seqs != B) return DN_EINVAL;
+  if (D % 8 != 0 || W < 1 || W > 4) return DN_EUNSUPPORTED;
+  const int64_t C = (int64_t)H * D, TT = (int64_t)B * T;
+  if (C >= ((int64_t)1 << 31) || (TT + 127) / 128 >= ((int64_t)1 << 31)) return DN_EUNSUPPORTED;  // grid
+  return DN_OK;
+}
+
+static dn::ConvParams conv_params(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                                  const int32_t *cu_seqlens) {
+  dn::ConvParams p = {};
+  p.cu = cu_seqlens;
+  p.TT = (int64_t)B * T;
+  p.T = T;
+  p.N = cu_seqlens ? n_seqs : B;
+  p.C = H * D;
+  p.W = W;
+  return p;
+}
+
+dn_status dn_short_conv(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs, int32_t dtype,
+                        const void *x, const float *w, const int32_t *cu_seqlens, void *y, hipStream_t stream) {
+  const dn_status st = conv_check(B, T, H, D, W, n_seqs, dtype, cu_seqlens);
+  if (st != DN_OK) return st;
+  if ((int64_t)B * T == 0) return DN_OK;
+  if (!x || !w || !y || !aligned16(x) || !aligned16(y)) return DN_EINVAL;
+  dn::ConvParams p = conv_params(B, T, H, D, W, n_seqs, cu_seqlens);
+  p.x = x;
+  p.w = w;
+  p.y = y;
+  return from_hip(dn::launch_conv(p, dtype, false, stream));
+}
+
+dn_status dn_short_conv_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                            int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
+                            const float *dy, float *dx, float *dw, hipStream_t stream) {
+  const dn_status st = conv_check(B, T, H, D, W, n_seqs, dtype, cu_seqlens);
+  if (st != DN_OK) return st;
+  if (!dw) return DN_EINVAL;
+  const bool empty = (int64_t)B * T == 0;
+  if (!empty && (!x || !w || !dy || !dx || !aligned16(x) || !aligned16(dy) || !aligned16(dx))) return DN_EINVAL;
+  dn::ConvParams p = conv_params(B, T, H, D, W, n_seqs, cu_seqlens);
+  p.x = x;
+  p.w = w;
+  p.dy = dy;
+  p.dx = dx;
+  p.dw = dw;
+  return from_hip(dn::launch_conv(p, dtype, true, stream));
+}
+
 }  // extern "C"

@@ -76,6 +76,20 @@ struct PrologueParams {
   int64_t rows;
 };
 
+// Depthwise causal short convolution over TT = B T tokens of C = H D channels
+// (x, y [TT][C] in the dtype; w, dw [C][W] fp32; dy, dx [TT][C] fp32)
+struct ConvParams {
+  const void *x;
+  const float *w;
+  const int32_t *cu;          // packed sequences, or null: sequences of T tokens
+  void *y;
+  const float *dy;
+  float *dx, *dw;
+  int64_t TT;
+  int T, N;                   // tokens per sequence (cu null); sequences (cu set)
+  int C, W;
+};
+
 struct SeqInfo {
   int b, t0, len;
 };
@@ -119,6 +133,8 @@ hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_stat
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
 hipError_t launch_longhorn(const LonghornParams &p, int dtype, int DK, hipStream_t stream);
 hipError_t launch_prologue(const PrologueParams &p, int dtype, int DK, bool backward, hipStream_t stream);
+// forward (y) or backward (dx, dw; dw is cleared first); W in 1..4
+hipError_t launch_conv(const ConvParams &p, int dtype, bool backward, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream);
 // ev_scan / ev_chunk (may be null) are recorded on `stream` after the scan and

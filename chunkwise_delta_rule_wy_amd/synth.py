@@ -177,6 +177,22 @@ def decode_inputs(B: int = 256, H: int = 32, Dk: int = 128, Dv: int = 128,
                 g=None if g is None else g.contiguous(), state=state.contiguous())
 
 
+def conv_inputs(B: int, T: int, H: int, D: int, W: int, dtype: torch.dtype = torch.bfloat16,
+                seed: int = 1200, lengths=None) -> dict:
+    """Inputs of the depthwise short convolution: a projection x ``[B,T,H,D]``
+    (N(0, 1), cast to dtype), taps w ``[H,D,W]`` (uniform in +-1/sqrt(W)), the
+    output gradient dy (N(0, 1), fp32) and, for packed sequences (B = 1, T =
+    sum(lengths)), cu_seqlens.  Draw order x, w, dy."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    if lengths is not None:
+        assert B == 1 and T == sum(lengths)
+    x = torch.randn(B, T, H, D, generator=gen)
+    w = (torch.rand(H, D, W, generator=gen) * 2 - 1) / W ** 0.5
+    dy = torch.randn(B, T, H, D, generator=gen)
+    return dict(x=x.to(dtype).contiguous(), w=w.contiguous(), dy=dy.contiguous(),
+                cu_seqlens=None if lengths is None else cu_seqlens_of(lengths))
+
+
 def rel_l2(x, y) -> float:
     """Relative L2 error ||x - y|| / ||y|| over a whole tensor, in fp64
     (absolute ||x|| when y is all zero)."""

@@ -300,6 +300,42 @@ dn_status dn_prologue_bwd(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t d
                           float *dq_in, float *dk_in, float *db_in, float *dx_in,
                           hipStream_t stream);
 
+/*
+ * Depthwise causal short convolution (the DeltaNet rebuttal, answer W2: the
+ * "short convolution" layers the layer applies beside the token mixer, here
+ * to any [B,T,H,D] projection).  Every channel (h, c) has its own W taps and
+ * a token sees itself and the W - 1 tokens before it in its own sequence:
+ *
+ *     y[t, h, c] = sum_{j < W} w[h, c, j] x[t - (W - 1) + j, h, c]
+ *
+ * with x = 0 before the sequence's first token (tap W - 1 is the current
+ * token).  The pages give neither the width nor an activation: the width is
+ * the caller's (1 to 4) and no activation is applied.  x, y [B,T,H,D] (dtype,
+ * 16-byte aligned; y may not alias x); w [H,D,W] fp32.  Packed sequences:
+ * cu_seqlens (device int32 [n_seqs + 1], as dn_chunk_fwd) with B == 1;
+ * otherwise cu_seqlens NULL and n_seqs == B.  T == 0 is a no-op.
+ * DN_EINVAL for bad sizes, dtype, null or misaligned pointers;
+ * DN_EUNSUPPORTED for D not a multiple of 8 or W outside 1..4.
+ */
+dn_status dn_short_conv(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                        int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
+                        void *y, hipStream_t stream);
+
+/*
+ * Backward of dn_short_conv, from dy = dL/dy [B,T,H,D] fp32:
+ *
+ *     dx[p, h, c] = sum_{j < W} w[h, c, j] dy[p + (W - 1) - j, h, c]   (outputs of p's sequence)
+ *     dw[h, c, j] = sum_p x[p, h, c] dy[p + (W - 1) - j, h, c]
+ *
+ * dx [B,T,H,D] fp32 (16-byte aligned), dw [H,D,W] fp32, both overwritten (dw
+ * is cleared on the stream first, then accumulated with atomic adds, so its
+ * summation order may differ between calls; with T == 0 it is set to zero).
+ * Other arguments and errors as dn_short_conv.
+ */
+dn_status dn_short_conv_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                            int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
+                            const float *dy, float *dx, float *dw, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

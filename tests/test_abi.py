@@ -293,3 +293,23 @@ def test_binding_checks_caller_workspaces():
         dn._workspace(torch.empty(64, dtype=torch.uint8)[::2], cpu, 8, "ws")
     with pytest.raises(ValueError):
         dn._workspace(ok, torch.device("cuda:0"), 8, "ws")  # on another device than the inputs
+
+
+def test_short_conv_validation(lib):
+    P = ctypes.c_void_p
+    f, fb = lib.dn_short_conv, lib.dn_short_conv_bwd
+    ok = [P(FAKE), P(FAKE), None, P(FAKE), None]  # x, w, cu, y, stream
+    assert f(1, 4, 2, 12, 4, 1, 1, *ok) == DN_EUNSUPPORTED   # D not a multiple of 8
+    assert f(1, 4, 2, 16, 5, 1, 1, *ok) == DN_EUNSUPPORTED   # W beyond 4
+    assert f(1, 4, 2, 16, 0, 1, 1, *ok) == DN_EUNSUPPORTED
+    assert f(2, 4, 2, 16, 4, 1, 1, *ok) == DN_EINVAL         # n_seqs != B without cu_seqlens
+    assert f(2, 4, 2, 16, 4, 2, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == DN_EINVAL  # packed needs B == 1
+    assert f(1, 4, 2, 16, 4, 1, 5, *ok) == DN_EINVAL         # dtype
+    assert f(1, 4, 2, 16, 4, 1, 1, P(FAKE + 8), P(FAKE), None, P(FAKE), None) == DN_EINVAL  # misaligned x
+    assert f(1, 4, 2, 16, 4, 1, 1, P(FAKE), None, None, P(FAKE), None) == DN_EINVAL
+    assert f(1, 0, 2, 16, 4, 1, 1, None, None, None, None, None) == DN_OK  # nothing to do
+    okb = [P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), None]  # x, w, cu, dy, dx, dw, stream
+    assert fb(1, 4, 2, 16, 4, 1, 0, *okb[:5], None, None) == DN_EINVAL  # dw is required
+    assert fb(1, 4, 2, 16, 4, 1, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE + 4), P(FAKE), None) == DN_EINVAL
+    assert fb(1, 4, 2, 24, 3, 1, 0, P(FAKE), P(FAKE), None, None, P(FAKE), P(FAKE), None) == DN_EINVAL
+    assert fb(1, 4, 2, 20, 3, 1, 0, *okb) == DN_EUNSUPPORTED

@@ -190,6 +190,8 @@ def main():
     wid = args.workload
     if wid == "dec":
         return bench_decode(args, dn, synth, dev)
+    if wid == "conv":
+        return bench_conv(args, dn, synth, dev)
     wid = int(wid)
     sh = synth.WORKLOADS[wid]
     backward = sh.backward
@@ -507,6 +509,47 @@ def bench_decode(args, dn, synth, dev):
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                    "traffic": None}}), flush=True)
+
+
+def bench_conv(args, dn, synth, dev):
+    """The short convolution (W = 4) over the q projection of the training
+    shape (B=4 T=4096 H=16 d=128, bf16): forward and backward per step."""
+    import torch
+    B, T, H, D, W = 4, 4096, 16, 128, 4
+    x = synth.conv_inputs(B, T, H, D, W, torch.bfloat16, seed=1250)
+    xd, wd, dyd = x["x"].to(dev), x["w"].to(dev), x["dy"].to(dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        dn.short_conv(xd, wd)
+        dn.short_conv_bwd(xd, wd, dyd)
+    torch.cuda.synchronize()
+    ev = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        dn.short_conv(xd, wd)
+        e[1].record(stream)
+        dn.short_conv_bwd(xd, wd, dyd)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fus = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3 / args.steps
+    bus = sum(e[1].elapsed_time(e[2]) for e in ev) * 1e3 / args.steps
+    n = B * T * H * D
+    fbytes = n * (2 + 2) + H * D * W * 4            # x read, y written (bf16), taps
+    bbytes = n * (2 + 4 + 4) + 2 * H * D * W * 4    # x, dy read, dx written, taps, dw
+    fg, bg = fbytes / (fus * 1e-6) / 1e9, bbytes / (bus * 1e-6) / 1e9
+    print(json.dumps({"metric": "short convolution fwd+bwd", "value": round(B * T / (ms * 1e-3), 1),
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+                      "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "short-conv-W4-B4-T4096-H16-d128"},
+                      "kernel_us": {"conv_fwd": round(fus, 2), "conv_bwd": round(bus, 2)},
+                      "roofline": {"bound": "hbm", "achieved": round(bg, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(bg / HBM_PEAK_GBS, 4), "traffic": None,
+                                   "kernel": "dn::conv_bwd_kernel", "bytes_per_launch": bbytes},
+                      "fwd_roofline": {"achieved": round(fg, 1), "frac": round(fg / HBM_PEAK_GBS, 4),
+                                       "bytes_per_launch": fbytes}}), flush=True)
 
 
 if __name__ == "__main__":

@@ -14,19 +14,23 @@
 // lane (bf16; two for fp32); the W - 1 tokens before the run (forward) or
 // after it (backward) are read again by the neighbouring wave.  Everything is
 // streamed once: the kernels are bound by HBM bandwidth.  In the backward pass
-// the four waves of a workgroup (four runs) add their weight-gradient partials
-// in LDS, and one wave adds the sum to dw with global atomics.
+// the eight waves of a workgroup (eight runs, 256 tokens) leave their
+// weight-gradient partials in LDS; the workgroup sums them and adds the sums
+// to dw with global atomics, consecutive threads on consecutive dw entries.
 #include "dn_rows.h"
 
 namespace dn {
 namespace {
 
-constexpr int CONV_THREADS = 256;  // four waves, one run each
-constexpr int CONV_RUN = 32;       // tokens per run
+constexpr int CONV_THREADS = 256;      // forward: four waves, one run each
+constexpr int CONV_BWD_THREADS = 512;  // backward: eight waves, one run each
+constexpr int CONV_RUN = 32;           // tokens per run
 constexpr int CONV_RUNS = CONV_THREADS / 64;
-constexpr int CONV_LANE_CH = 8;    // channels per lane
+constexpr int CONV_BWD_RUNS = CONV_BWD_THREADS / 64;
+constexpr int CONV_LANE_CH = 8;        // channels per lane
 constexpr int CONV_WAVE_CH = 64 * CONV_LANE_CH;
-constexpr int CONV_BATCH = 8;      // token rows loaded ahead of use
+constexpr int CONV_BATCH = 8;          // token rows loaded ahead of use (forward)
+constexpr int CONV_BWD_BATCH = 4;      // the same for the backward pass (x and dy rows)
 
 // the sequence around token t: [st, nx)
 struct SeqTrack {
@@ -162,11 +166,12 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_fwd_kernel(ConvParams p) {
 }
 
 template <typename E, int W>
-__global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvParams p) {
-  __shared__ float part[CONV_RUNS][W][CONV_LANE_CH][64];
+__global__ __launch_bounds__(CONV_BWD_THREADS) void conv_bwd_kernel(ConvParams p) {
+  constexpr int PART = W * CONV_LANE_CH * 64;  // partials of one wave: [j][e][lane]
+  __shared__ float part[CONV_BWD_RUNS][PART];
   const int lane = threadIdx.x & 63, run = threadIdx.x >> 6;
   const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * CONV_LANE_CH;
-  const int64_t t0 = ((int64_t)blockIdx.y * CONV_RUNS + run) * CONV_RUN;
+  const int64_t t0 = ((int64_t)blockIdx.y * CONV_BWD_RUNS + run) * CONV_RUN;
   const bool act = c0 < p.C;
   float dwa[W][CONV_LANE_CH];
 #pragma unroll
@@ -186,10 +191,10 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvParams p) {
     }
     SeqTrack sq;
     sq.init(p, t0);
-    for (int b = 0; b < CONV_RUN; b += CONV_BATCH) {
-      float xb[CONV_BATCH][CONV_LANE_CH], db[CONV_BATCH][CONV_LANE_CH];
+    for (int b = 0; b < CONV_RUN; b += CONV_BWD_BATCH) {
+      float xb[CONV_BWD_BATCH][CONV_LANE_CH], db[CONV_BWD_BATCH][CONV_LANE_CH];
 #pragma unroll
-      for (int i = 0; i < CONV_BATCH; ++i) {
+      for (int i = 0; i < CONV_BWD_BATCH; ++i) {
         const int64_t t = t0 + b + i, u = t + (W - 1);
         if (act && t < t1) load8<E>(x + t * p.C + c0, xb[i]);
         else zero8(xb[i]);
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvParams p) {
         else zero8(db[i]);
       }
 #pragma unroll
-      for (int i = 0; i < CONV_BATCH; ++i) {
+      for (int i = 0; i < CONV_BWD_BATCH; ++i) {
         const int64_t t = t0 + b + i;
         if (t >= t1) break;
         sq.advance(t);
@@ -226,23 +231,23 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvParams p) {
       }
     }
   }
-  // weight gradient: the four runs' partials summed in LDS, then one atomic
-  // add per (channel, tap) and workgroup
+  // weight gradient: the eight runs' partials summed in LDS, then one atomic
+  // add per (channel, tap) and workgroup; thread i takes entry i of the
+  // workgroup's contiguous slice of dw (channel i / W, tap i % W)
 #pragma unroll
   for (int j = 0; j < W; ++j)
 #pragma unroll
-    for (int e = 0; e < CONV_LANE_CH; ++e) part[run][j][e][lane] = dwa[j][e];
+    for (int e = 0; e < CONV_LANE_CH; ++e) part[run][(j * CONV_LANE_CH + e) * 64 + lane] = dwa[j][e];
   __syncthreads();
-  if (run == 0 && act) {
+  const int64_t cbase = (int64_t)blockIdx.x * CONV_WAVE_CH;
+  for (int i = threadIdx.x; i < PART; i += CONV_BWD_THREADS) {
+    const int cl = i / W, j = i % W;
+    if (cbase + cl >= p.C) break;
+    const int src = (j * CONV_LANE_CH + (cl % CONV_LANE_CH)) * 64 + cl / CONV_LANE_CH;
+    float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < W; ++j)
-#pragma unroll
-      for (int e = 0; e < CONV_LANE_CH; ++e) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < CONV_RUNS; ++r) s += part[r][j][e][lane];
-        atomicAdd(p.dw + (c0 + e) * W + j, s);
-      }
+    for (int r = 0; r < CONV_BWD_RUNS; ++r) s += part[r][src];
+    atomicAdd(p.dw + cbase * W + i, s);
   }
 }
 
@@ -253,14 +258,15 @@ __global__ __launch_bounds__(256) void conv_zero_kernel(float *dst, int64_t n) {
 
 template <typename E, int W>
 hipError_t launch_w(const ConvParams &p, bool backward, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.C + CONV_WAVE_CH - 1) / CONV_WAVE_CH),
-                  (unsigned)((p.TT + CONV_RUN * CONV_RUNS - 1) / (CONV_RUN * CONV_RUNS)));
+  const unsigned gx = (unsigned)((p.C + CONV_WAVE_CH - 1) / CONV_WAVE_CH);
+  const int64_t span = (int64_t)CONV_RUN * (backward ? CONV_BWD_RUNS : CONV_RUNS);
+  const dim3 grid(gx, (unsigned)((p.TT + span - 1) / span));
   if (backward) {
     const int64_t n = (int64_t)p.C * W;
     hipLaunchKernelGGL(conv_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.dw, n);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || p.TT == 0) return err;
-    hipLaunchKernelGGL((conv_bwd_kernel<E, W>), grid, dim3(CONV_THREADS), 0, stream, p);
+    hipLaunchKernelGGL((conv_bwd_kernel<E, W>), grid, dim3(CONV_BWD_THREADS), 0, stream, p);
   } else {
     if (p.TT == 0) return hipSuccess;
     hipLaunchKernelGGL((conv_fwd_kernel<E, W>), grid, dim3(CONV_THREADS), 0, stream, p);

@@ -94,6 +94,10 @@ def load_library():
     lib.dn_short_conv.restype = ctypes.c_int
     lib.dn_short_conv_bwd.argtypes = [ctypes.c_int32] * 7 + [P] * 6 + [P]
     lib.dn_short_conv_bwd.restype = ctypes.c_int
+    lib.dn_short_conv_l2.argtypes = [ctypes.c_int32] * 7 + [P] * 4 + [P]
+    lib.dn_short_conv_l2.restype = ctypes.c_int
+    lib.dn_short_conv_l2_bwd.argtypes = [ctypes.c_int32] * 7 + [P] * 6 + [P]
+    lib.dn_short_conv_l2_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -427,27 +431,32 @@ def _conv_dims(x, w, cu_seqlens):
     return B, T, H, D, W, n_seqs
 
 
-def short_conv(x, w, cu_seqlens=None):
+def short_conv(x, w, cu_seqlens=None, l2norm: bool = False):
     """Depthwise causal short convolution (``dn_short_conv``): y[t] = sum_j
     w[:, :, j] x[t - (W - 1) + j] inside each sequence; x [B, T, H, D], w
-    [H, D, W] float32.  Returns y (dtype of x)."""
+    [H, D, W] float32.  With ``l2norm`` every (token, head) row of y is
+    scaled to unit length in the same pass (``dn_short_conv_l2``).  Returns y
+    (dtype of x)."""
     lib = load_library()
     B, T, H, D, W, n = _conv_dims(x, w, cu_seqlens)
     y = torch.empty_like(x)
-    _check("dn_short_conv", lib.dn_short_conv(
+    fn = "dn_short_conv_l2" if l2norm else "dn_short_conv"
+    _check(fn, getattr(lib, fn)(
         B, T, H, D, W, n, _DTYPES[x.dtype], _ptr(x), _ptr(w), _ptr(cu_seqlens), _ptr(y), _stream(x.device)))
     return y
 
 
-def short_conv_bwd(x, w, dy, cu_seqlens=None):
-    """Backward of ``short_conv`` (``dn_short_conv_bwd``): float32 (dx, dw)
-    from dy = dL/dy (float32, the shape of x)."""
+def short_conv_bwd(x, w, dy, cu_seqlens=None, l2norm: bool = False):
+    """Backward of ``short_conv`` (``dn_short_conv_bwd``, or
+    ``dn_short_conv_l2_bwd`` with ``l2norm``): float32 (dx, dw) from dy =
+    dL/dy (float32, the shape of x)."""
     lib = load_library()
     B, T, H, D, W, n = _conv_dims(x, w, cu_seqlens)
     _need(dy, "dy", torch.float32, tuple(x.shape), x.device)
     dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     dw = torch.empty(w.shape, dtype=torch.float32, device=x.device)
-    _check("dn_short_conv_bwd", lib.dn_short_conv_bwd(
+    fn = "dn_short_conv_l2_bwd" if l2norm else "dn_short_conv_bwd"
+    _check(fn, getattr(lib, fn)(
         B, T, H, D, W, n, _DTYPES[x.dtype], _ptr(x), _ptr(w), _ptr(cu_seqlens), _ptr(dy), _ptr(dx),
         _ptr(dw), _stream(x.device)))
     return dx, dw

@@ -498,4 +498,39 @@ dn_status dn_short_conv_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t 
   return from_hip(dn::launch_conv(p, dtype, true, stream));
 }
 
+dn_status dn_short_conv_l2(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                           int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens, void *y,
+                           hipStream_t stream) {
+  const dn_status st = conv_check(B, T, H, D, W, n_seqs, dtype, cu_seqlens);
+  if (st != DN_OK) return st;
+  if (D != 64 && D != 128) return DN_EUNSUPPORTED;
+  if ((int64_t)B * T == 0) return DN_OK;
+  if (!x || !w || !y || !aligned16(x) || !aligned16(y)) return DN_EINVAL;
+  dn::ConvParams p = conv_params(B, T, H, D, W, n_seqs, cu_seqlens);
+  p.x = x;
+  p.w = w;
+  p.y = y;
+  p.norm_lanes = D / 8;
+  return from_hip(dn::launch_conv(p, dtype, false, stream));
+}
+
+dn_status dn_short_conv_l2_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                               int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
+                               const float *dy, float *dx, float *dw, hipStream_t stream) {
+  const dn_status st = conv_check(B, T, H, D, W, n_seqs, dtype, cu_seqlens);
+  if (st != DN_OK) return st;
+  if (D != 64 && D != 128) return DN_EUNSUPPORTED;
+  if (!dw) return DN_EINVAL;
+  const bool empty = (int64_t)B * T == 0;
+  if (!empty && (!x || !w || !dy || !dx || !aligned16(x) || !aligned16(dy) || !aligned16(dx))) return DN_EINVAL;
+  dn::ConvParams p = conv_params(B, T, H, D, W, n_seqs, cu_seqlens);
+  p.x = x;
+  p.w = w;
+  p.dy = dy;
+  p.dx = dx;
+  p.dw = dw;
+  p.norm_lanes = D / 8;
+  return from_hip(dn::launch_conv(p, dtype, true, stream));
+}
+
 }  // extern "C"

@@ -88,6 +88,7 @@ struct ConvParams {
   int64_t TT;
   int T, N;                   // tokens per sequence (cu null); sequences (cu set)
   int C, W;
+  int norm_lanes;             // 0, or D / 8: L2-normalise every (token, head) row of D channels
 };
 
 struct SeqInfo {

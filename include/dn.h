@@ -336,6 +336,31 @@ dn_status dn_short_conv_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t 
                             int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
                             const float *dy, float *dx, float *dw, hipStream_t stream);
 
+/*
+ * dn_short_conv fused with the L2 normalisation of dn_prologue: every
+ * (token, head) row of the convolution's output z is scaled to unit length,
+ *
+ *     y[t, h, :] = z[t, h, :] / |z[t, h, :]|     (a zero row stays zero)
+ *
+ * in the same pass, which is how a (Gated) DeltaNet layer prepares q and k
+ * from their projections (the rebuttal's short convolutions, then the
+ * workloads' normalisation).  D in {64, 128}; otherwise as dn_short_conv.
+ */
+dn_status dn_short_conv_l2(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                           int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
+                           void *y, hipStream_t stream);
+
+/*
+ * Backward of dn_short_conv_l2 from dy = dL/dy (fp32): z is recomputed from x
+ * and w, dz = (dy - u (u . dy)) / |z| with u = z / |z| (0 for a zero row),
+ * then dx and dw are those of dn_short_conv_bwd for dz.  Arguments, output
+ * semantics (dw cleared, then accumulated atomically) and errors as
+ * dn_short_conv_bwd; D in {64, 128}.
+ */
+dn_status dn_short_conv_l2_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
+                               int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,
+                               const float *dy, float *dx, float *dw, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

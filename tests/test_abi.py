@@ -313,3 +313,14 @@ def test_short_conv_validation(lib):
     assert fb(1, 4, 2, 16, 4, 1, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE + 4), P(FAKE), None) == DN_EINVAL
     assert fb(1, 4, 2, 24, 3, 1, 0, P(FAKE), P(FAKE), None, None, P(FAKE), P(FAKE), None) == DN_EINVAL
     assert fb(1, 4, 2, 20, 3, 1, 0, *okb) == DN_EUNSUPPORTED
+
+
+def test_short_conv_l2_validation(lib):
+    P = ctypes.c_void_p
+    f, fb = lib.dn_short_conv_l2, lib.dn_short_conv_l2_bwd
+    assert f(1, 4, 2, 32, 4, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED  # D not 64 or 128
+    assert f(1, 4, 2, 128, 5, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED
+    assert f(1, 4, 2, 128, 4, 1, 1, P(FAKE + 8), P(FAKE), None, P(FAKE), None) == DN_EINVAL
+    assert f(1, 0, 2, 128, 4, 1, 1, None, None, None, None, None) == DN_OK
+    assert fb(1, 4, 2, 64, 4, 1, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None, None) == DN_EINVAL
+    assert fb(1, 4, 2, 256, 4, 1, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED

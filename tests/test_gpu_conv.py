@@ -103,3 +103,54 @@ def test_conv_full_size_packed_sampled(oracle_lib):
     from chunkwise_delta_rule_wy_amd.synth import VARLEN_LENGTHS
     inp = conv_inputs(1, sum(VARLEN_LENGTHS), 32, 128, 4, torch.bfloat16, seed=1251, lengths=list(VARLEN_LENGTHS))
     check(oracle_lib, inp, heads=[3, 31])
+
+
+def l2_reference(oracle_lib, x, w, dy, cu):
+    """The fused pass as a composition of the oracle's pinned functions: the
+    convolution, then the prologue's row normalisation (and their backward)."""
+    z = oracle_lib.short_conv(x, w, cu)
+    zeros = np.zeros(z.shape[:3])
+    y = oracle_lib.prologue(z, z, zeros)[0]
+    dz = oracle_lib.prologue_bwd(z, z, zeros, None, 1.0, dy, dy, zeros)[0]
+    dx, dw = oracle_lib.short_conv_bwd(x, w, dz, cu)
+    return y, dx, dw
+
+
+def check_l2(oracle_lib, inp, heads=None):
+    x, w, dy, cu = inp["x"], inp["w"], inp["dy"], inp["cu_seqlens"]
+    d = lambda t: None if t is None else t.to(DEV)
+    y = dn.short_conv(d(x), d(w), d(cu), l2norm=True)
+    dx, dw = dn.short_conv_bwd(d(x), d(w), d(dy), d(cu), l2norm=True)
+    torch.cuda.synchronize()
+    y, dx, dw = y.cpu(), dx.cpu(), dw.cpu()
+    if heads is not None:
+        x, w, dy = x[:, :, heads], w[heads], dy[:, :, heads]
+        y, dx, dw = y[:, :, heads], dx[:, :, heads], dw[heads]
+    ry, rdx, rdw = l2_reference(oracle_lib, x, w, dy, cu)
+    ey, edx, edw = rel_l2(y, ry), rel_l2(dx, rdx), rel_l2(dw, rdw)
+    print("l2 rel-L2 y %.2e dx %.2e dw %.2e" % (ey, edx, edw), flush=True)
+    assert ey <= YTOL[x.dtype]
+    assert edx <= 1e-5
+    assert edw <= 1e-5
+    return y, dx, dw
+
+
+@pytest.mark.parametrize("W", [1, 2, 4])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_conv_l2_parity(oracle_lib, W, D, dtype):
+    inp = conv_inputs(2, 150, 5, D, W, dtype, seed=1260 + W + D)
+    inp["w"][3] = 0.0  # head 3 convolves to zero rows: they stay zero, with zero gradients
+    y, dx, dw = check_l2(oracle_lib, inp)
+    assert torch.count_nonzero(y[:, :, 3]).item() == 0 and torch.count_nonzero(dx[:, :, 3]).item() == 0
+    n = y[:, :, :3].double().norm(dim=-1)
+    assert (n - 1).abs().max().item() < 1e-2  # unit rows (bf16 rounding included)
+
+
+def test_conv_l2_packed(oracle_lib):
+    lengths = [37, 0, 1, 130, 5, 64, 2]
+    check_l2(oracle_lib, conv_inputs(1, sum(lengths), 4, 128, 4, torch.bfloat16, seed=1270, lengths=lengths))
+
+
+def test_conv_l2_full_size_sampled(oracle_lib):
+    check_l2(oracle_lib, conv_inputs(4, 4096, 16, 128, 4, torch.bfloat16, seed=1271), heads=[1, 14])

@@ -513,7 +513,9 @@ def bench_decode(args, dn, synth, dev):
 
 def bench_conv(args, dn, synth, dev):
     """The short convolution (W = 4) over the q projection of the training
-    shape (B=4 T=4096 H=16 d=128, bf16): forward and backward per step."""
+    shape (B=4 T=4096 H=16 d=128, bf16): forward and backward per step (the
+    timed steps); then the same with the L2 normalisation fused in, timed by
+    its events only."""
     import torch
     B, T, H, D, W = 4, 4096, 16, 128, 4
     x = synth.conv_inputs(B, T, H, D, W, torch.bfloat16, seed=1250)
@@ -535,6 +537,20 @@ def bench_conv(args, dn, synth, dev):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     fus = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3 / args.steps
     bus = sum(e[1].elapsed_time(e[2]) for e in ev) * 1e3 / args.steps
+    # the same with the per-head L2 normalisation fused in (how q and k are prepared)
+    for _ in range(args.warmup):
+        dn.short_conv(xd, wd, l2norm=True)
+        dn.short_conv_bwd(xd, wd, dyd, l2norm=True)
+    ev2 = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+    for e in ev2:
+        e[0].record(stream)
+        dn.short_conv(xd, wd, l2norm=True)
+        e[1].record(stream)
+        dn.short_conv_bwd(xd, wd, dyd, l2norm=True)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    lfus = sum(e[0].elapsed_time(e[1]) for e in ev2) * 1e3 / args.steps
+    lbus = sum(e[1].elapsed_time(e[2]) for e in ev2) * 1e3 / args.steps
     n = B * T * H * D
     fbytes = n * (2 + 2) + H * D * W * 4            # x read, y written (bf16), taps
     bbytes = n * (2 + 4 + 4) + 2 * H * D * W * 4    # x, dy read, dx written, taps, dw
@@ -544,7 +560,8 @@ def bench_conv(args, dn, synth, dev):
                       "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
                       "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "short-conv-W4-B4-T4096-H16-d128"},
-                      "kernel_us": {"conv_fwd": round(fus, 2), "conv_bwd": round(bus, 2)},
+                      "kernel_us": {"conv_fwd": round(fus, 2), "conv_bwd": round(bus, 2),
+                                    "conv_l2_fwd": round(lfus, 2), "conv_l2_bwd": round(lbus, 2)},
                       "roofline": {"bound": "hbm", "achieved": round(bg, 1), "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": round(bg / HBM_PEAK_GBS, 4), "traffic": None,
                                    "kernel": "dn::conv_bwd_kernel", "bytes_per_launch": bbytes},

@@ -8,7 +8,10 @@ when y is stored in bf16; dx within 1e-6; dw, a sum over every token in
 fp32, within 1e-5.  Cases span several 32-token runs and 512-channel groups
 with ragged tails, packed sequences with empty and one-token members, every
 width 1..4, and the training shapes (B=4 T=4096 H=16 d=128, and the packed
-65536-token, H=32 input) with the oracle on sampled heads.
+65536-token, H=32 input) with the oracle on sampled heads.  The variant fused
+with the per-head L2 normalisation is compared with the oracle's convolution
+followed by its prologue normalisation, and a whole layer (projections through
+the convolutions, the chunkwise passes and back) with the oracle's composition.
 """
 import numpy as np
 import pytest
@@ -154,3 +157,49 @@ def test_conv_l2_packed(oracle_lib):
 
 def test_conv_l2_full_size_sampled(oracle_lib):
     check_l2(oracle_lib, conv_inputs(4, 4096, 16, 128, 4, torch.bfloat16, seed=1271), heads=[1, 14])
+
+
+def test_layer_composition(oracle_lib):
+    """Projections to gradients through the library: q, k by the fused
+    convolution and normalisation, v by the plain convolution, the chunkwise
+    forward and backward (bf16), then the convolutions' backward; against the
+    same composition of the oracle's functions in fp64 (relative L2 2e-2, the
+    bf16 recurrence's bar)."""
+    B, T, H, D, W = 2, 150, 2, 64, 4
+    xq = conv_inputs(B, T, H, D, W, torch.bfloat16, seed=1280)
+    xk = conv_inputs(B, T, H, D, W, torch.bfloat16, seed=1281)
+    xv = conv_inputs(B, T, H, D, W, torch.bfloat16, seed=1282)
+    gen = torch.Generator("cpu").manual_seed(1283)
+    beta = torch.sigmoid(torch.randn(B, T, H, generator=gen))
+    g = -0.1 * torch.nn.functional.softplus(torch.randn(B, T, H, generator=gen))
+    dO = torch.randn(B, T, H, D, generator=gen).to(torch.bfloat16)
+    dv_ = lambda t: t.to(DEV)
+    q = dn.short_conv(dv_(xq["x"]), dv_(xq["w"]), l2norm=True)
+    k = dn.short_conv(dv_(xk["x"]), dv_(xk["w"]), l2norm=True)
+    v = dn.short_conv(dv_(xv["x"]), dv_(xv["w"]))
+    o, hT = dn.chunk_fwd(q, k, v, dv_(beta), dv_(g), None)
+    gr = dn.chunk_bwd(q, k, v, dv_(beta), dv_(g), None, dv_(dO))
+    dxq, dwq = dn.short_conv_bwd(dv_(xq["x"]), dv_(xq["w"]), gr["dq"], l2norm=True)
+    dxk, dwk = dn.short_conv_bwd(dv_(xk["x"]), dv_(xk["w"]), gr["dk"], l2norm=True)
+    dxv, dwv = dn.short_conv_bwd(dv_(xv["x"]), dv_(xv["w"]), gr["dv"])
+    torch.cuda.synchronize()
+
+    zeros = np.zeros((B, T, H))
+    zq = oracle_lib.short_conv(xq["x"], xq["w"])
+    zk = oracle_lib.short_conv(xk["x"], xk["w"])
+    rq = oracle_lib.prologue(zq, zq, zeros)[0]
+    rk = oracle_lib.prologue(zk, zk, zeros)[0]
+    rv = oracle_lib.short_conv(xv["x"], xv["w"])
+    ro, _ = oracle_lib.fwd(rq, rk, rv, beta, g, None)
+    rg = oracle_lib.bwd(rq, rk, rv, beta, g, None, dO, None)
+    rdzq = oracle_lib.prologue_bwd(zq, zq, zeros, None, 1.0, rg["dq"], rg["dq"], zeros)[0]
+    rdzk = oracle_lib.prologue_bwd(zk, zk, zeros, None, 1.0, rg["dk"], rg["dk"], zeros)[0]
+    rdxq, rdwq = oracle_lib.short_conv_bwd(xq["x"], xq["w"], rdzq)
+    rdxk, rdwk = oracle_lib.short_conv_bwd(xk["x"], xk["w"], rdzk)
+    rdxv, rdwv = oracle_lib.short_conv_bwd(xv["x"], xv["w"], rg["dv"])
+    errs = {"o": rel_l2(o.cpu(), ro), "dxq": rel_l2(dxq.cpu(), rdxq), "dwq": rel_l2(dwq.cpu(), rdwq),
+            "dxk": rel_l2(dxk.cpu(), rdxk), "dwk": rel_l2(dwk.cpu(), rdwk), "dxv": rel_l2(dxv.cpu(), rdxv),
+            "dwv": rel_l2(dwv.cpu(), rdwv), "dbeta": rel_l2(gr["dbeta"].cpu(), rg["dbeta"]),
+            "dg": rel_l2(gr["dg"].cpu(), rg["dg"])}
+    print({k_: "%.2e" % e for k_, e in errs.items()}, flush=True)
+    assert max(errs.values()) <= 2e-2

@@ -501,3 +501,27 @@ def delta_rule(q, k, v, beta, g=None, h0=None, cu_seqlens=None, save_states=True
     ``save_states`` keeps the chunk states from the forward pass for the
     backward pass (bfloat16 inputs) instead of recomputing them."""
     return DeltaRule.apply(q, k, v, beta, g, h0, cu_seqlens, save_states)
+
+
+class ShortConv(torch.autograd.Function):
+    """Autograd wrapper of the depthwise causal short convolution: forward by
+    ``short_conv``, backward by ``short_conv_bwd`` (dx cast to x's dtype, dw
+    float32).  ``l2norm`` fuses the per-head L2 normalisation (q and k)."""
+
+    @staticmethod
+    def forward(ctx, x, w, cu_seqlens, l2norm=False):
+        ctx.save_for_backward(x, w, cu_seqlens)
+        ctx.l2norm = l2norm
+        return short_conv(x, w, cu_seqlens, l2norm=l2norm)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w, cu = ctx.saved_tensors
+        dx, dw = short_conv_bwd(x, w, dy.float().contiguous(), cu, l2norm=ctx.l2norm)
+        return dx.to(x.dtype), dw, None, None
+
+
+def short_conv_fn(x, w, cu_seqlens=None, l2norm=False):
+    """Differentiable short convolution (optionally with the per-head L2
+    normalisation fused in)."""
+    return ShortConv.apply(x, w, cu_seqlens, l2norm)

@@ -203,3 +203,19 @@ def test_layer_composition(oracle_lib):
             "dg": rel_l2(gr["dg"].cpu(), rg["dg"])}
     print({k_: "%.2e" % e for k_, e in errs.items()}, flush=True)
     assert max(errs.values()) <= 2e-2
+
+
+@pytest.mark.parametrize("l2norm", [False, True])
+def test_conv_autograd(oracle_lib, l2norm):
+    inp = conv_inputs(2, 70, 3, 64, 3, torch.float32, seed=1290)
+    x = inp["x"].to(DEV).requires_grad_(True)
+    w = inp["w"].to(DEV).requires_grad_(True)
+    dy = inp["dy"].to(DEV)
+    y = dn.short_conv_fn(x, w, l2norm=l2norm)
+    (y * dy).sum().backward()
+    torch.cuda.synchronize()
+    if l2norm:
+        _, rdx, rdw = l2_reference(oracle_lib, inp["x"], inp["w"], inp["dy"], None)
+    else:
+        rdx, rdw = oracle_lib.short_conv_bwd(inp["x"], inp["w"], inp["dy"])
+    assert rel_l2(x.grad.cpu(), rdx) <= 1e-5 and rel_l2(w.grad.cpu(), rdw) <= 1e-5

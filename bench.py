@@ -209,11 +209,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     mk = TimingEvent
     nev = max(args.steps, 1) + max(args.cold_steps, 0)
-    fev = [(mk(), mk()) for _ in range(nev)]
-    bev = [[mk() for _ in range(4)] for _ in range(nev)] if backward else None
-
     longhorn = args.variant == "longhorn"
     saved = backward and args.bwd_mode == "saved"
+    fev = [(mk(), mk()) for _ in range(nev)]
+    # the saved-state backward starts where the forward ends (nothing runs in
+    # between): its first two events are not recorded and the forward's end
+    # event starts the scan, four records per step instead of six
+    bev = ([[None, None, mk(), mk()] if saved else [mk() for _ in range(4)] for _ in range(nev)]
+           if backward else None)
     if backward and args.chunk != 64:
         print("the backward pass runs 64-token chunks only", file=sys.stderr)
         sys.exit(2)
@@ -296,7 +299,8 @@ def main():
             for j, name in enumerate(("recompute", "state_grad_scan", "chunk_grad")):
                 if j == 0 and saved:
                     continue  # the forward pass stored the states
-                t[name] = us([(bev[i][j], bev[i][j + 1]) for i in idx])
+                start = (lambda i: fev[i][1]) if (j == 1 and saved) else (lambda i: bev[i][j])
+                t[name] = us([(start(i), bev[i][j + 1]) for i in idx])
             if longhorn and not saved:
                 t["longhorn_eps_bwd"] = us([lev[i] for i in idx])
             if args.prologue and not (saved and not longhorn):

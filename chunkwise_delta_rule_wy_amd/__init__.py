@@ -207,7 +207,8 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     may be passed to avoid an allocation per call.  ``events``: four
     ``torch.cuda.Event(enable_timing=True)`` that the library records before
     its first kernel and after the recompute, the state-gradient sweep and the
-    chunk-gradient kernel (``dn_chunk_bwd_events``).  ``saved``: skip the
+    chunk-gradient kernel (``dn_chunk_bwd_events``); a None entry is not
+    recorded.  ``saved``: skip the
     recompute and read the states that ``chunk_fwd(..., save_workspace=
     workspace)`` stored for these inputs (``dn_chunk_bwd_saved``).
     ``prologue_inputs`` = (q_in, k_in, x_in, gate_scale), with ``saved``: q, k,
@@ -249,11 +250,11 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     ev = None
     if events is not None:
         if len(events) != 4:
-            raise ValueError("events: four torch.cuda.Event objects expected")
+            raise ValueError("events: four torch.cuda.Event objects (or None) expected")
         for e in events:
-            if e.cuda_event == 0:  # torch creates the event on its first record
+            if e is not None and e.cuda_event == 0:  # torch creates the event on its first record
                 e.record(torch.cuda.current_stream(dev))
-        ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        ev = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
     if longhorn_beta is not None:
         if not saved or prologue_inputs is not None:
             raise ValueError("longhorn_beta needs saved=True and no prologue_inputs")

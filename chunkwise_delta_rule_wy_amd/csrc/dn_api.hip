@@ -152,7 +152,7 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   TrainWs w;
   st = train_ws(s, cu_seqlens, workspace, workspace_bytes, stream, w);
   if (st != DN_OK) return st;
-  if (events && hipEventRecord(events[0], stream) != hipSuccess) return DN_EHIP;
+  if (events && events[0] && hipEventRecord(events[0], stream) != hipSuccess) return DN_EHIP;
 
   // 1. forward sweep that stores every chunk-start state
   dn::FwdParams fp = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
@@ -162,7 +162,7 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
     hipError_t e = dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
     if (e != hipSuccess) return DN_EHIP;
   }
-  if (events && hipEventRecord(events[1], stream) != hipSuccess) return DN_EHIP;
+  if (events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) return DN_EHIP;
 
   // 2. reverse sweep for the state gradients, 3. chunk-parallel token gradients
   dn::BwdParams bp = {};

@@ -121,8 +121,9 @@ dn_status dn_chunk_bwd(const dn_shape *s,
  * state-gradient sweep and events[3] after the chunk-gradient kernel (whose
  * launch follows the sweep directly), so that hipEventElapsedTime on
  * consecutive pairs gives each stage's device time.  The four events are
- * created (with timing enabled) and owned by the caller; events == NULL is
- * dn_chunk_bwd.  A failed record returns DN_EHIP.
+ * created (with timing enabled) and owned by the caller; a NULL entry is
+ * not recorded, and events == NULL is dn_chunk_bwd.  A failed record returns
+ * DN_EHIP.
  */
 dn_status dn_chunk_bwd_events(const dn_shape *s,
                               const void *q, const void *k, const void *v,

@@ -271,3 +271,20 @@ def test_varlen_all_empty(saved):
     assert o.numel() == 0 and torch.equal(hT.cpu(), x["h0"])
     gr = gpu_bwd(x, saved)
     assert torch.equal(gr["dh0"], x["dhT"])
+
+
+def test_partial_stage_events():
+    # a None entry of the four stage events is not recorded; the others time their stages
+    sh = Shape(2, 200, 2, 128, 128, torch.bfloat16, gated=True, has_h0=True, backward=True)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in make_inputs(sh, seed=1310).items()}
+    ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv), dtype=torch.uint8, device=DEV)
+    dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], save_workspace=ws)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"])
+    ref = dn.chunk_bwd(*args, workspace=ws, saved=True)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    out = dn.chunk_bwd(*args, workspace=ws, saved=True, events=[None, None, e[1], e[2]])
+    torch.cuda.synchronize()
+    assert e[0].elapsed_time(e[1]) > 0 and e[1].elapsed_time(e[2]) > 0
+    for k in ("dq", "dk", "dv", "dbeta", "dg", "dh0"):
+        assert torch.equal(out[k], ref[k]), k

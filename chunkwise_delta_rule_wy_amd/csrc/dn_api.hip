@@ -452,7 +452,8 @@ static dn_status conv_check(int32_t B, int32_t T, int32_t H, int32_t D, int32_t 
   if (cu_seqlens ? (B != 1 || n_seqs < 1) : n_seqs != B) return DN_EINVAL;
   if (D % 8 != 0 || W < 1 || W > 4) return DN_EUNSUPPORTED;
   const int64_t C = (int64_t)H * D, TT = (int64_t)B * T;
-  if (C >= ((int64_t)1 << 31) || (TT + 127) / 128 >= ((int64_t)1 << 31)) return DN_EUNSUPPORTED;  // grid
+  // grid: token blocks of 128 on x (< 2^31), channel groups of 512 on y (<= 65535)
+  if ((C + 511) / 512 > 65535 || (TT + 127) / 128 >= ((int64_t)1 << 31)) return DN_EUNSUPPORTED;
   return DN_OK;
 }
 

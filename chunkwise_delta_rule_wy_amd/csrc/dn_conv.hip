@@ -128,8 +128,8 @@ __device__ __forceinline__ void normalise_row(float (&z)[CONV_LANE_CH]) {
 template <typename E, int W, int NL>
 __global__ __launch_bounds__(CONV_THREADS) void conv_fwd_kernel(ConvParams p) {
   const int lane = threadIdx.x & 63, run = threadIdx.x >> 6;
-  const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * CONV_LANE_CH;
-  const int64_t t0 = ((int64_t)blockIdx.y * CONV_RUNS + run) * CONV_RUN;
+  const int64_t c0 = ((int64_t)blockIdx.y * 64 + lane) * CONV_LANE_CH;
+  const int64_t t0 = ((int64_t)blockIdx.x * CONV_RUNS + run) * CONV_RUN;
   if (t0 >= p.TT) return;  // the whole wave
   const bool act = c0 < p.C;
   const int64_t t1 = min(t0 + (int64_t)CONV_RUN, p.TT);
@@ -196,7 +196,7 @@ __device__ __forceinline__ void dw_flush(const ConvParams &p, float (*part)[W * 
 #pragma unroll
     for (int e = 0; e < CONV_LANE_CH; ++e) part[run][(j * CONV_LANE_CH + e) * 64 + lane] = dwa[j][e];
   __syncthreads();
-  const int64_t cbase = (int64_t)blockIdx.x * CONV_WAVE_CH;
+  const int64_t cbase = (int64_t)blockIdx.y * CONV_WAVE_CH;
   for (int i = threadIdx.x; i < PART; i += CONV_BWD_THREADS) {
     const int cl = i / W, j = i % W;
     if (cbase + cl >= p.C) break;
@@ -213,8 +213,8 @@ __global__ __launch_bounds__(CONV_BWD_THREADS) void conv_bwd_kernel(ConvParams p
   constexpr int PART = W * CONV_LANE_CH * 64;  // partials of one wave: [j][e][lane]
   __shared__ float part[CONV_BWD_RUNS][PART];
   const int lane = threadIdx.x & 63, run = threadIdx.x >> 6;
-  const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * CONV_LANE_CH;
-  const int64_t t0 = ((int64_t)blockIdx.y * CONV_BWD_RUNS + run) * CONV_RUN;
+  const int64_t c0 = ((int64_t)blockIdx.y * 64 + lane) * CONV_LANE_CH;
+  const int64_t t0 = ((int64_t)blockIdx.x * CONV_BWD_RUNS + run) * CONV_RUN;
   const bool act = c0 < p.C;
   float dwa[W][CONV_LANE_CH];
 #pragma unroll
@@ -287,8 +287,8 @@ __global__ __launch_bounds__(CONV_BWD_THREADS) void conv_l2_bwd_kernel(ConvParam
   constexpr int PART = W * CONV_LANE_CH * 64;
   __shared__ float part[CONV_BWD_RUNS][PART];
   const int lane = threadIdx.x & 63, run = threadIdx.x >> 6;
-  const int64_t c0 = ((int64_t)blockIdx.x * 64 + lane) * CONV_LANE_CH;
-  const int64_t t0 = ((int64_t)blockIdx.y * CONV_BWD_RUNS + run) * CONV_RUN;
+  const int64_t c0 = ((int64_t)blockIdx.y * 64 + lane) * CONV_LANE_CH;
+  const int64_t t0 = ((int64_t)blockIdx.x * CONV_BWD_RUNS + run) * CONV_RUN;
   const bool act = c0 < p.C;
   float dwa[W][CONV_LANE_CH];
 #pragma unroll
@@ -395,9 +395,10 @@ __global__ __launch_bounds__(256) void conv_zero_kernel(float *dst, int64_t n) {
 
 template <typename E, int W>
 hipError_t launch_w(const ConvParams &p, bool backward, hipStream_t stream) {
-  const unsigned gx = (unsigned)((p.C + CONV_WAVE_CH - 1) / CONV_WAVE_CH);
+  // token blocks on x (up to 2^31 - 1), channel groups of 512 on y
+  const unsigned gy = (unsigned)((p.C + CONV_WAVE_CH - 1) / CONV_WAVE_CH);
   const int64_t span = (int64_t)CONV_RUN * (backward ? CONV_BWD_RUNS : CONV_RUNS);
-  const dim3 grid(gx, (unsigned)((p.TT + span - 1) / span));
+  const dim3 grid((unsigned)((p.TT + span - 1) / span), gy);
   if (backward) {
     const int64_t n = (int64_t)p.C * W;
     hipLaunchKernelGGL(conv_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p.dw, n);

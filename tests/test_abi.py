@@ -324,3 +324,11 @@ def test_short_conv_l2_validation(lib):
     assert f(1, 0, 2, 128, 4, 1, 1, None, None, None, None, None) == DN_OK
     assert fb(1, 4, 2, 64, 4, 1, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None, None) == DN_EINVAL
     assert fb(1, 4, 2, 256, 4, 1, 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), None) == DN_EUNSUPPORTED
+
+
+def test_short_conv_grid_limits(lib):
+    # channel groups of 512 sit on the grid's y axis (at most 65535 of them); tokens on x
+    P = ctypes.c_void_p
+    f = lib.dn_short_conv
+    assert f(1, 4, 262144, 128, 4, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED
+    assert f(1, 4, 262143, 128, 4, 1, 1, None, P(FAKE), None, P(FAKE), None) == DN_EINVAL  # in range: x checked next

@@ -331,4 +331,5 @@ def test_short_conv_grid_limits(lib):
     P = ctypes.c_void_p
     f = lib.dn_short_conv
     assert f(1, 4, 262144, 128, 4, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED
-    assert f(1, 4, 262143, 128, 4, 1, 1, None, P(FAKE), None, P(FAKE), None) == DN_EINVAL  # in range: x checked next
+    assert f(1, 4, 262141, 128, 4, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED
+    assert f(1, 4, 262140, 128, 4, 1, 1, None, P(FAKE), None, P(FAKE), None) == DN_EINVAL  # 65535 groups: x checked next

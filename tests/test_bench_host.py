@@ -1,0 +1,39 @@
+"""Host-side checks of the benchmark's accounting and contract (no GPU):
+the algorithmic bytes it divides by the measured times, counted here tensor by
+tensor, and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from chunkwise_delta_rule_wy_amd import synth  # noqa: E402
+
+
+def test_chunk_gradient_bytes_per_chunk_head():
+    # per token and head at dk = 128, dv = 256: q, k, v, dO in bf16, beta and g in
+    # fp32 read; dq, dk, dv, dbeta, dg in fp32 written; per (chunk, head) the bf16
+    # chunk state h and its gradient dh (dk x dv each)
+    read = 128 * 2 + 128 * 2 + 256 * 2 + 256 * 2 + 4 + 4
+    written = 128 * 4 + 128 * 4 + 256 * 4 + 4 + 4
+    per_chunk_head = 64 * (read + written) + 2 * 128 * 256 * 2
+    assert per_chunk_head == 361472
+    assert bench.chunk_grad_bytes(synth.WORKLOADS[4]) == per_chunk_head * 4096
+
+
+def test_forward_bytes():
+    # gated forward B4 T4096 H16 dk128 dv256: q, k, v in bf16, beta, g, h0 read;
+    # o in bf16 and hT written
+    th = 4 * 4096 * 16
+    state = 4 * 16 * 128 * 256 * 4
+    expect = th * (2 * 128 * 2 + 256 * 2 + 8) + th * 256 * 2 + 2 * state
+    assert bench.workload_bytes(synth.WORKLOADS[3], False) == expect
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

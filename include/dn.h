@@ -20,8 +20,8 @@
  * ---------------------------------------
  * - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *   never allocates, frees, or synchronises; each call enqueues its kernels on
- *   `stream` and returns.  Inputs are read-only (except the decode `state`,
- *   updated in place).  There is no global mutable state: calls are
+ *   `stream` and returns.  Inputs are read-only (except the decode `state`
+ *   and dn_longhorn_eps_bwd's `dk`, updated in place).  There is no global mutable state: calls are
  *   thread-safe; calls sharing a workspace on different streams race.
  * - Layouts are dense row-major:
  *     q, k        [B, T, H, Dk]       v, o, dO    [B, T, H, Dv]
@@ -330,8 +330,8 @@ dn_status dn_short_conv(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, i
  *
  * dx [B,T,H,D] fp32 (16-byte aligned), dw [H,D,W] fp32, both overwritten (dw
  * is cleared on the stream first, then accumulated with atomic adds, so its
- * summation order may differ between calls; with T == 0 it is set to zero).
- * Other arguments and errors as dn_short_conv.
+ * summation order may differ between calls; with T == 0 it is set to zero);
+ * neither may alias an input.  Other arguments and errors as dn_short_conv.
  */
 dn_status dn_short_conv_bwd(int32_t B, int32_t T, int32_t H, int32_t D, int32_t W, int32_t n_seqs,
                             int32_t dtype, const void *x, const float *w, const int32_t *cu_seqlens,

@@ -37,6 +37,9 @@ CHUNK_GRAD_TRAFFIC_W4 = 1511.6e6
 # the same for the forward kernel at the gated forward-only workload (B=4 T=4096
 # H=16 dk=128 dv=256): 294.0 MB read + 142.6 MB written
 FWD_TRAFFIC_W3 = 436.6e6
+# the same for the short convolution's backward kernel (W = 4, B=4 T=4096 H=16 d=128,
+# bf16): 214.3 MB read + 136.3 MB written
+CONV_BWD_TRAFFIC = 350.7e6
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
 PROBE_LIB = os.path.join(ROOT, "chunkwise_delta_rule_wy_amd", "libdnprobe.so")
 _probe = None
@@ -555,6 +558,11 @@ def bench_conv(args, dn, synth, dev):
     torch.cuda.synchronize()
     lfus = sum(e[0].elapsed_time(e[1]) for e in ev2) * 1e3 / args.steps
     lbus = sum(e[1].elapsed_time(e[2]) for e in ev2) * 1e3 / args.steps
+    if args.copy_calibration:  # the kernel of known size for the byte counters
+        a = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+        torch.empty_like(a).copy_(a)
+        torch.cuda.synchronize()
+        del a
     n = B * T * H * D
     fbytes = n * (2 + 2) + H * D * W * 4            # x read, y written (bf16), taps
     bbytes = n * (2 + 4 + 4) + 2 * H * D * W * 4    # x, dy read, dx written, taps, dw
@@ -567,8 +575,9 @@ def bench_conv(args, dn, synth, dev):
                       "kernel_us": {"conv_fwd": round(fus, 2), "conv_bwd": round(bus, 2),
                                     "conv_l2_fwd": round(lfus, 2), "conv_l2_bwd": round(lbus, 2)},
                       "roofline": {"bound": "hbm", "achieved": round(bg, 1), "peak": HBM_PEAK_GBS,
-                                   "unit": "GB/s", "frac": round(bg / HBM_PEAK_GBS, 4), "traffic": None,
-                                   "kernel": "dn::conv_bwd_kernel", "bytes_per_launch": bbytes},
+                                   "unit": "GB/s", "frac": round(bg / HBM_PEAK_GBS, 4),
+                                   "traffic": CONV_BWD_TRAFFIC, "kernel": "dn::conv_bwd_kernel",
+                                   "bytes_per_launch": bbytes},
                       "fwd_roofline": {"achieved": round(fg, 1), "frac": round(fg / HBM_PEAK_GBS, 4),
                                        "bytes_per_launch": fbytes}}), flush=True)
 

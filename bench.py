@@ -180,8 +180,9 @@ def main():
                          "Longhorn row, computed (and differentiated) around the same passes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(every (sequence, head) pair is independent; see DESIGN.md for sharding)",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(every (sequence, head) pair is independent, so several GPUs would each take a "
+              "share of the pairs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -344,14 +344,18 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     }
     st<bf16x4>(ob + RS::O_M + 512 * m_block(TI, TJ) + lb.m, cvt4(v));
   };
+  // in the scan, wave 0 (which also keeps the scale bookkeeping) hands block
+  // (3, 0) to wave 2, the prep wave with the least other work there
   if constexpr (PW == 0) {
     mtile(I1{}, I0{});
     mtile(I2{}, I0{});
-    mtile(I3{}, I0{});
+    if constexpr (MODE != MODE_SCAN) mtile(I3{}, I0{});
   } else if constexpr (PW == 1) {
     mtile(I2{}, I1{});
     mtile(I3{}, I1{});
     mtile(I3{}, I2{});
+  } else if constexpr (PW == 2 && MODE == MODE_SCAN) {
+    mtile(I3{}, I0{});
   }
 
   iss(2);

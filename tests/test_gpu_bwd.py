@@ -2,15 +2,18 @@
 sequential adjoint, through the C ABI.
 
 Every gradient (dq, dk, dv, dbeta, dg, dh0) must be within relative L2 2e-2
-of the oracle (bf16 inputs, fp32 gradients), over the whole tensor.
+of the oracle (bf16 inputs, fp32 gradients), over the whole tensor and over
+every (sequence, head) pair, and within 2.5 times that over every 64-token
+chunk of every pair (tests/parity.py).  The full-size workloads are compared
+on every pair, in both backward modes.
 """
-import numpy as np
 import pytest
 import torch
 
 import chunkwise_delta_rule_wy_amd as dn
+import parity
 from chunkwise_delta_rule_wy_amd import synth
-from chunkwise_delta_rule_wy_amd.synth import Shape, make_inputs, rel_l2
+from chunkwise_delta_rule_wy_amd.synth import Shape, make_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -44,16 +47,7 @@ def check_bwd(x, oracle_lib, label, saved=False):
     gr = gpu_bwd(x, saved)
     ref = oracle_lib.bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["dO"], x["dhT"],
                          cu_seqlens=x["cu_seqlens"])
-    errs = {}
-    for name in NAMES:
-        if ref[name] is None:
-            assert gr[name] is None
-            continue
-        assert torch.isfinite(gr[name]).all(), name
-        errs[name] = rel_l2(gr[name], ref[name])
-    print(label, " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
-    for name, e in errs.items():
-        assert e <= TOL, (name, e)
+    parity.check_grads(gr, ref, x["cu_seqlens"], TOL, label)
     return gr
 
 
@@ -67,6 +61,10 @@ CASES = [
     (1, 129, 9, 128, 64, True, False),
     (1, 130, 1, 128, 1024, True, True),   # the largest d_v, ragged tail
     (2, 70, 1, 64, 1024, False, True),
+    # N*H a multiple of 8: the XCD-aware workgroup placement of the full-size shapes
+    (2, 200, 4, 128, 256, True, True),
+    (4, 130, 4, 128, 128, False, True),
+    (2, 77, 8, 64, 192, True, False),
 ]
 
 
@@ -84,6 +82,14 @@ def test_bwd_varlen_ragged(oracle_lib):
     gr = check_bwd(x, oracle_lib, "varlen")
     # an empty sequence passes its state gradient through
     assert torch.equal(gr["dh0"][4], x["dhT"][4])
+
+
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_bwd_varlen_xcd_placement(oracle_lib, saved):
+    # 4 packed sequences x 4 heads (N*H = 16, the XCD-aware placement), d_v 256
+    lens = (200, 65, 1, 130)
+    sh = Shape(1, sum(lens), 4, 128, 256, torch.bfloat16, True, True, backward=True, lengths=lens)
+    check_bwd(make_inputs(sh, seed=43), oracle_lib, "varlen N*H=16", saved)
 
 
 def test_bwd_no_final_state_gradient(oracle_lib):
@@ -136,57 +142,32 @@ def test_autograd_wrapper_matches_entry_points():
     assert torch.equal(q.grad, gr["dq"].to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
-def test_bwd_full_size_sampled(oracle_lib, saved):
-    sh = synth.WORKLOADS[4]
-    x = synth.workload_inputs(4)
-    gr = gpu_bwd(x, saved)
-    for name in NAMES:
-        assert torch.isfinite(gr[name]).all(), name
-    rng = np.random.default_rng(4)
-    for idx in rng.choice(sh.B * sh.H, size=3, replace=False):
-        b, h = int(idx) // sh.H, int(idx) % sh.H
-        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
-        st = lambda t: t[b:b + 1, h:h + 1].contiguous()
-        ref = oracle_lib.bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["g"]),
-                             st(x["h0"]), sl(x["dO"]), st(x["dhT"]))
-        errs = {}
-        for name in NAMES:
-            mine = gr[name][b:b + 1, :, h:h + 1] if name != "dh0" else gr[name][b:b + 1, h:h + 1]
-            errs[name] = rel_l2(mine, ref[name])
-        print("workload 4 pair (%d,%d)" % (b, h), " ".join("%s %.2e" % kv for kv in errs.items()),
-              flush=True)
-        for name, e in errs.items():
-            assert e <= TOL, (name, e)
-
-
-@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
-def test_bwd_varlen_full_size_sampled(oracle_lib, saved):
-    """Packed workload (8 sequences, 65536 tokens, H=32, d=128) in one call;
-    three (sequence, head) pairs of the shorter sequences, which sit after the
-    first in the packing and end in partial chunks, against the oracle."""
-    sh = synth.WORKLOADS[6]
-    x = synth.workload_inputs(6)
-    gr = gpu_bwd(x, saved)
-    for name in NAMES:
-        assert torch.isfinite(gr[name]).all(), name
-    cu = x["cu_seqlens"].tolist()
-    rng = np.random.default_rng(6)
-    for n in (1, 6, 7):
-        h = int(rng.integers(sh.H))
-        t0, t1 = cu[n], cu[n + 1]
-        sl = lambda t: t[:, t0:t1, h:h + 1].contiguous()
-        st = lambda t: t[n:n + 1, h:h + 1].contiguous()
-        ref = oracle_lib.bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["g"]),
-                             st(x["h0"]), sl(x["dO"]), st(x["dhT"]))
-        errs = {}
-        for name in NAMES:
-            mine = gr[name][n:n + 1, h:h + 1] if name == "dh0" else gr[name][:, t0:t1, h:h + 1]
-            errs[name] = rel_l2(mine, ref[name])
-        print("packed workload seq %d (%d tokens) head %d" % (n, t1 - t0, h),
-              " ".join("%s %.2e" % kv for kv in errs.items()), flush=True)
-        for name, e in errs.items():
-            assert e <= TOL, (name, e)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid,saved", [(4, False), (4, True), (6, False), (6, True)],
+                         ids=["w4-recompute", "w4-saved", "w6-recompute", "w6-saved"])
+def test_bwd_full_size_every_pair(oracle_lib, wid, saved):
+    """The training workloads at full size (workload 4; the packed workload 6,
+    8 sequences of 65536 tokens with H=32, d=128, in one call), in the launch
+    configuration the benchmark times: every gradient of every (sequence,
+    head) pair and every chunk against the oracle, both backward modes."""
+    x, (oo, ho), ref = parity.oracle_run(oracle_lib, wid)
+    if saved:
+        # the saved-state pair's forward outputs too
+        d = to_dev(x)
+        sh = synth.WORKLOADS[wid]
+        ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv, sh.n_seqs),
+                         dtype=torch.uint8, device=DEV)
+        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"],
+                             save_workspace=ws)
+        gr = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
+                          d["cu_seqlens"], workspace=ws, saved=True)
+        torch.cuda.synchronize()
+        parity.check_fwd_outputs(o.cpu(), hT.cpu(), oo, ho, x["cu_seqlens"], TOL, "workload %d saving fwd" % wid)
+        del d, ws, o, hT
+        gr = {k: (None if v is None else v.cpu()) for k, v in gr.items()}
+    else:
+        gr = gpu_bwd(x, False)
+    parity.check_grads(gr, ref, x["cu_seqlens"], TOL, "workload %d %s" % (wid, "saved" if saved else "recompute"))
 
 
 SAVED_CASES = [
@@ -253,9 +234,7 @@ def test_strong_decay_parity(oracle_lib, saved):
     o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"])
     torch.cuda.synchronize()
     oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"])
-    eo, eh = rel_l2(o.cpu(), oo), rel_l2(hT.cpu(), ho)
-    print("strong decay forward rel-L2 o %.2e hT %.2e" % (eo, eh), flush=True)
-    assert eo <= TOL and eh <= TOL
+    parity.check_fwd_outputs(o.cpu(), hT.cpu(), oo, ho, None, TOL, "strong decay forward")
     check_bwd(x, oracle_lib, "strong decay", saved)
 
 

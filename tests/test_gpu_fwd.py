@@ -1,17 +1,19 @@
 """GPU parity of the chunkwise forward pass and the decode step against the
 fp64 oracle, through the C ABI.
 
-Tolerances (relative L2 over a whole output tensor): 1e-4 for fp32 inputs and
-2e-2 for bf16 inputs, on o and on the final state.  The oracle reads exactly
-the bits the GPU reads (bf16 values upcast to fp64).
+Tolerances (relative L2): 1e-4 for fp32 inputs and 2e-2 for bf16 inputs, on o
+and on the final state, over the whole tensor and over every (sequence, head)
+pair, and 2.5 times that over every 64-token chunk of every pair
+(tests/parity.py).  The oracle reads exactly the bits the GPU reads (bf16
+values upcast to fp64).  The full-size workloads are compared on every pair.
 """
 import ctypes
 
-import numpy as np
 import pytest
 import torch
 
 import chunkwise_delta_rule_wy_amd as dn
+import parity
 from chunkwise_delta_rule_wy_amd import synth
 from chunkwise_delta_rule_wy_amd.synth import Shape, make_inputs, rel_l2
 
@@ -31,14 +33,16 @@ def gpu_fwd(x):
     return o.cpu(), hT.cpu()
 
 
-def check_fwd(x, dtype, oracle_lib, label=""):
-    o, hT = gpu_fwd(x)
+def check_fwd(x, dtype, oracle_lib, label="", chunk=64):
+    if chunk == 64:
+        o, hT = gpu_fwd(x)
+    else:
+        d = to_dev(x)
+        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"], chunk=chunk)
+        torch.cuda.synchronize()
+        o, hT = o.cpu(), hT.cpu()
     oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["cu_seqlens"])
-    eo, eh = rel_l2(o, oo), rel_l2(hT, ho)
-    print("%s rel-L2 o %.3e hT %.3e" % (label, eo, eh), flush=True)
-    assert np.isfinite(o.float().numpy()).all()
-    assert eo <= TOL[dtype], eo
-    assert eh <= TOL[dtype], eh
+    parity.check_fwd_outputs(o, hT, oo, ho, x["cu_seqlens"], TOL[dtype], label)
     return o, hT
 
 
@@ -54,6 +58,11 @@ SMALL = [
     (1, 65, 9, 128, 128, torch.bfloat16, True, True),   # N*H not a multiple of 8
     (1, 130, 1, 128, 1024, torch.bfloat16, True, True),  # the largest d_v, ragged tail
     (1, 100, 1, 64, 1024, torch.float32, True, True),    # the largest d_v in fp32
+    # N*H a multiple of 8: the XCD-aware workgroup placement of the full-size shapes
+    (2, 200, 4, 128, 256, torch.bfloat16, True, True),
+    (4, 130, 4, 128, 128, torch.bfloat16, False, False),
+    (2, 77, 8, 64, 192, torch.bfloat16, True, True),
+    (2, 150, 4, 64, 64, torch.float32, True, True),
 ]
 
 
@@ -81,6 +90,13 @@ def test_fwd_varlen_ragged(oracle_lib):
                   g=x["g"][:, s:e].contiguous(), h0=x["h0"][n:n + 1].contiguous(), cu_seqlens=None)
         on, hn = gpu_fwd(xs)
         assert torch.equal(on, o[:, s:e]) and torch.equal(hn[0], hT[n])
+
+
+def test_fwd_varlen_xcd_placement(oracle_lib):
+    # 4 packed sequences x 4 heads (N*H = 16, the XCD-aware placement), d_v 256
+    lens = (200, 65, 1, 130)
+    sh = Shape(1, sum(lens), 4, 128, 256, torch.bfloat16, True, True, lengths=lens)
+    check_fwd(make_inputs(sh, seed=23), torch.bfloat16, oracle_lib, "varlen N*H=16")
 
 
 def test_fwd_zero_length(oracle_lib):
@@ -116,27 +132,30 @@ def test_fwd_orthonormal_keys_recall(oracle_lib):
     assert rel_l2(recall.T, v[0, :, 0]) < 1e-4
 
 
-def test_fwd_deterministic_and_state_passing():
+def test_fwd_deterministic_and_state_passing(oracle_lib):
     sh = Shape(2, 333, 2, 128, 256, torch.bfloat16, True, True)
     x = make_inputs(sh, seed=11)
     o1, h1 = gpu_fwd(x)
     for _ in range(3):
         o2, h2 = gpu_fwd(x)
         assert torch.equal(o1, o2) and torch.equal(h1, h2)
-    # Split at a chunk boundary: two segments equal one run up to rounding.  The
-    # kernel carries the state scaled by a running product of decays and feeds
-    # it to the MFMA in bf16, so the two runs round it differently: they agree
-    # to the bf16 level, far inside the parity tolerance.
+    # Split at a chunk boundary: each segment against the oracle run on the same
+    # segment (the second from the first's GPU final state), and the two
+    # segments together against one run.  The kernel carries the state scaled by
+    # a running product of decays and feeds it to the MFMA in bf16, so the two
+    # runs round it differently: they must agree to within one bf16 epsilon
+    # (2^-8, about 4e-3).
     T1 = 128
-    xa = {kk: (vv[:, :T1].contiguous() if kk in ("q", "k", "v", "beta", "g") else vv)
-          for kk, vv in x.items()}
-    oa, ha = gpu_fwd(xa)
-    xb = {kk: (vv[:, T1:].contiguous() if kk in ("q", "k", "v", "beta", "g") else vv)
-          for kk, vv in x.items()}
+    seg = lambda a, b: {kk: (vv[:, a:b].contiguous() if kk in ("q", "k", "v", "beta", "g") else vv)
+                        for kk, vv in x.items()}
+    xa = seg(0, T1)
+    oa, ha = check_fwd(xa, torch.bfloat16, oracle_lib, "segment 1")
+    xb = seg(T1, None)
     xb["h0"] = ha
-    ob, hb = gpu_fwd(xb)
-    assert rel_l2(hb, h1) < 1e-2
-    assert rel_l2(torch.cat([oa, ob], 1), o1) < 1e-2
+    ob, hb = check_fwd(xb, torch.bfloat16, oracle_lib, "segment 2")
+    eh, eo = rel_l2(hb, h1), rel_l2(torch.cat([oa, ob], 1), o1)
+    print("chained vs one run: o %.2e hT %.2e" % (eo, eh), flush=True)
+    assert eh < 4e-3 and eo < 4e-3, (eo, eh)
 
 
 def test_fwd_canary_no_out_of_bounds_writes():
@@ -178,9 +197,9 @@ def test_step_parity(oracle_lib, B, H, Dk, Dv, dtype, gated):
     o = dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], st)
     torch.cuda.synchronize()
     oo, so = oracle_lib.step(x["q"], x["k"], x["v"], x["beta"], x["g"], x["state"])
-    eo, es = rel_l2(o.cpu(), oo), rel_l2(st.cpu(), so)
-    print("decode rel-L2 o %.3e state %.3e" % (eo, es), flush=True)
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    # whole tensor and every (batch, head) pair
+    parity.check("o", parity.state_errors(o.cpu().unsqueeze(-1), oo[..., None]), TOL[dtype], "decode")
+    parity.check("state", parity.state_errors(st.cpu(), so), TOL[dtype], "decode")
 
 
 def test_decode_steps_equal_chunk_forward():
@@ -201,36 +220,16 @@ def test_decode_steps_equal_chunk_forward():
 
 
 # ------------------------------------------------------- full-size workloads
-def sample_pairs(N, H, k, seed):
-    rng = np.random.default_rng(seed)
-    idx = rng.choice(N * H, size=min(k, N * H), replace=False)
-    return [(int(i) // H, int(i) % H) for i in idx]
-
-
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("wid", [2, 3, 5])
-def test_fwd_full_size_sampled(oracle_lib, wid):
+def test_fwd_full_size_every_pair(oracle_lib, wid):
+    """The forward workloads at full size, in the launch configuration the
+    benchmark times: every (sequence, head) pair and every chunk against the
+    oracle."""
     sh = synth.WORKLOADS[wid]
-    x = synth.workload_inputs(wid)
+    x, (oo, ho), _ = parity.oracle_run(oracle_lib, wid)
     o, hT = gpu_fwd(x)
-    assert np.isfinite(o.float().numpy()).all()
-    cu = x["cu_seqlens"]
-    pairs = sample_pairs(sh.n_seqs, sh.H, 6, wid)
-    if wid == 5:
-        # the longest sequence, plus a random sample
-        pairs = [(2, 0)] + pairs[:4]
-    for n, h in pairs:
-        if cu is None:
-            b, s, e = n, 0, sh.T
-        else:
-            b, s, e = 0, int(cu[n]), int(cu[n + 1])
-        sl = lambda t: t[b:b + 1, s:e, h:h + 1].contiguous()
-        oo, ho = oracle_lib.fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]),
-                                None if x["g"] is None else sl(x["g"]),
-                                None if x["h0"] is None else x["h0"][n:n + 1, h:h + 1].contiguous())
-        eo = rel_l2(o[b, s:e, h], oo[0, :, 0])
-        eh = rel_l2(hT[n, h], ho[0, 0])
-        print("workload %d pair (%d,%d) rel-L2 o %.3e hT %.3e" % (wid, n, h, eo, eh), flush=True)
-        assert eo <= TOL[sh.dtype] and eh <= TOL[sh.dtype]
+    parity.check_fwd_outputs(o, hT, oo, ho, x["cu_seqlens"], TOL[sh.dtype], "workload %d" % wid)
 
 
 # ----------------------------------------------------------- 32-token chunks
@@ -243,6 +242,8 @@ C32_CASES = [
     (1, 1, 2, 128, 128, True, True),
     (2, 95, 2, 64, 192, True, False),
     (1, 130, 1, 128, 1024, True, True),
+    (2, 200, 4, 128, 256, True, True),    # N*H = 8
+    (4, 97, 4, 128, 128, False, False),   # N*H = 16
 ]
 
 
@@ -253,46 +254,27 @@ def test_fwd_chunk32_parity(oracle_lib, cfg):
     B, T, H, Dk, Dv, gated, h0 = cfg
     sh = Shape(B, T, H, Dk, Dv, torch.bfloat16, gated, h0)
     x = make_inputs(sh, seed=300 + T + Dv)
-    d = to_dev(x)
-    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], chunk=32)
-    torch.cuda.synchronize()
-    oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"])
-    eo, eh = rel_l2(o.cpu(), oo), rel_l2(hT.cpu(), ho)
-    print("chunk 32 %s rel-L2 o %.3e hT %.3e" % (cfg, eo, eh), flush=True)
-    assert eo <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16], (eo, eh)
+    check_fwd(x, torch.bfloat16, oracle_lib, "chunk 32 %s" % (cfg,), chunk=32)
 
 
 def test_fwd_chunk32_varlen_ragged(oracle_lib):
     lens = (1, 31, 32, 33, 0, 100, 5)
     sh = Shape(1, sum(lens), 2, 128, 128, torch.bfloat16, True, True, lengths=lens)
     x = make_inputs(sh, seed=333)
+    o, hT = check_fwd(x, torch.bfloat16, oracle_lib, "chunk 32 varlen", chunk=32)
+    # the empty sequence passes its state through
+    assert torch.equal(hT[4], x["h0"][4])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_fwd_chunk32_full_size_every_pair(oracle_lib, wid):
+    """The forward workloads at full size with 32-token chunks: every
+    (sequence, head) pair and every chunk against the oracle."""
+    sh = synth.WORKLOADS[wid]
+    x, (oo, ho), _ = parity.oracle_run(oracle_lib, wid)
     d = to_dev(x)
     o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"], chunk=32)
     torch.cuda.synchronize()
-    oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["cu_seqlens"])
-    eo, eh = rel_l2(o.cpu(), oo), rel_l2(hT.cpu(), ho)
-    print("chunk 32 varlen rel-L2 o %.3e hT %.3e" % (eo, eh), flush=True)
-    assert eo <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16], (eo, eh)
-    # the empty sequence passes its state through
-    assert torch.equal(hT[4].cpu(), x["h0"][4])
-
-
-@pytest.mark.parametrize("wid", [2, 3])
-def test_fwd_chunk32_full_size_sampled(oracle_lib, wid):
-    """The forward workloads at full size with 32-token chunks: three
-    (batch, head) pairs against the oracle."""
-    sh = synth.WORKLOADS[wid]
-    x = synth.workload_inputs(wid)
-    d = to_dev(x)
-    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], chunk=32)
-    torch.cuda.synchronize()
-    o, hT = o.cpu(), hT.cpu()
-    rng = np.random.default_rng(32 + wid)
-    for idx in rng.choice(sh.B * sh.H, size=3, replace=False):
-        b, h = int(idx) // sh.H, int(idx) % sh.H
-        sl = lambda t: None if t is None else t[b:b + 1, :, h:h + 1].contiguous()
-        st = lambda t: None if t is None else t[b:b + 1, h:h + 1].contiguous()
-        oo, ho = oracle_lib.fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["g"]), st(x["h0"]))
-        eo, eh = rel_l2(o[b:b + 1, :, h:h + 1], oo), rel_l2(hT[b:b + 1, h:h + 1], ho)
-        print("chunk 32 workload %d pair (%d,%d) rel-L2 o %.3e hT %.3e" % (wid, b, h, eo, eh), flush=True)
-        assert eo <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16], (eo, eh)
+    parity.check_fwd_outputs(o.cpu(), hT.cpu(), oo, ho, x["cu_seqlens"], TOL[sh.dtype],
+                             "chunk 32 workload %d" % wid)

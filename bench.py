@@ -114,16 +114,30 @@ def workload_bytes(sh, backward: bool) -> float:
 
 
 def chunk_grad_bytes(sh) -> float:
-    """Algorithmic HBM bytes of one launch of the chunk-gradient kernel: per
-    (chunk, head) it reads q, k, v, dO, beta, g and the two bf16 chunk states
-    (h and dh, d_k x d_v each) and writes dq, dk, dv, dbeta, dg in fp32."""
+    """Algorithmic HBM bytes of one launch of the chunk-gradient kernel: one
+    read of each of its inputs (q, k, v, dO, beta, g) and one write of each of
+    its outputs (dq, dk, dv, dbeta, dg in fp32) at their dtypes.  The bf16
+    chunk states h and dh it also reads are intermediates of the backward
+    pass and are not counted (they appear in the measured traffic)."""
     es = 2 if str(sh.dtype).endswith("bfloat16") else 4
     th = sh.B * sh.T * sh.H
-    lengths = sh.lengths if sh.lengths is not None else [sh.T] * sh.B
-    chunk_heads = sum((L + 63) // 64 for L in lengths) * sh.H
     per_tok = (2 * sh.Dk * es + 2 * sh.Dv * es + 4 * (2 if sh.gated else 1)
                + 2 * sh.Dk * 4 + sh.Dv * 4 + 4 * (2 if sh.gated else 1))
-    return float(th * per_tok + chunk_heads * 2 * sh.Dk * sh.Dv * 2)
+    return float(th * per_tok)
+
+
+def chunk_state_bytes(sh) -> float:
+    """Bytes of the bf16 chunk states h and dh (d_k x d_v per (chunk, head)
+    each) that the chunk-gradient kernel reads besides its inputs."""
+    lengths = sh.lengths if sh.lengths is not None else [sh.T] * sh.B
+    chunk_heads = sum((L + 63) // 64 for L in lengths) * sh.H
+    return float(chunk_heads * 2 * sh.Dk * sh.Dv * 2)
+
+
+def decode_bytes(B=256, H=32, Dk=128, Dv=128) -> float:
+    """Algorithmic bytes of one decode step: the fp32 state read and written,
+    q, k, v read and o written in bf16, beta and g read in fp32."""
+    return float(B * H * Dk * Dv * 4 * 2 + B * H * (2 * Dk + 2 * Dv) * 2 + B * H * 8)
 
 
 def bwd_flops(sh) -> float:
@@ -161,6 +175,9 @@ def main():
                     help="after the timed steps, this many more steps each preceded by a 1 GiB "
                          "write that evicts the L2s and the 256 MB Infinity Cache; their per-kernel "
                          "event times are reported as kernel_us_cold (median, min)")
+    ap.add_argument("--no-forward-configs", action="store_true",
+                    help="skip the forward-only workloads and the decode step that the default "
+                         "(training) run times after its own steps")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the probes of the machine's own peaks (HBM copy bandwidth, a bf16 "
                          "MFMA loop, the shader clock) reported beside the vendor figures")
@@ -330,7 +347,13 @@ def main():
                else None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kname, "kernel_us": round(kus, 2), "bytes_per_launch": kbytes}
+                "kernel": kname, "kernel_us": round(kus, 2), "bytes_per_launch": kbytes,
+                "timing": "warm: mean of the kernel's live event times over the timed steps, "
+                          "which run back to back on resident inputs"}
+    if traffic is not None:
+        roofline["traffic_over_algorithmic"] = round(traffic / kbytes, 3)
+    if backward:
+        roofline["chunk_state_bytes"] = chunk_state_bytes(sh)
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     out = {
@@ -360,6 +383,10 @@ def main():
     if cold_t:
         out["kernel_us_cold"] = {k: {"median": round(med(v), 2), "min": round(min(v), 2)}
                                  for k, v in cold_t.items()}
+        ck = "chunk_grad" if backward else "fwd"
+        cmed = med(cold_t[ck])
+        roofline["frac_cold"] = round(kbytes / (cmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        roofline["kernel_us_cold_median"] = round(cmed, 2)
     if not args.no_measured_peaks:
         mp = measured_peaks(torch, dev, stream)
         if mp is not None:
@@ -378,7 +405,98 @@ def main():
         del a, b
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, sh, backward, args.cpu_seconds, args.variant)
+    if not args.no_forward_configs and wid == 4 and not args.prologue and args.variant == "delta":
+        del d, ws, x
+        torch.cuda.empty_cache()
+        out["forward_configs"] = forward_configs(dn, synth, dev, stream)
     print(json.dumps(out), flush=True)
+
+
+# Algorithmic HBM floors of the forward workloads at 8 TB/s (one read of every
+# input and one write of every output): the denominators of their roofline
+# fractions
+FWD_WORKLOADS = (2, 3, 5)
+
+
+def _cold_times(fn, stream, reps=20, warm=5):
+    """The cold protocol: `warm` untimed calls, then `reps` calls, each after a
+    1 GiB write that evicts the L2s and the 256 MB Infinity Cache, timed by
+    events on the launch stream.  Returns the list of times (us)."""
+    import torch
+    scratch = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=torch.device("cuda:0"))
+    for _ in range(warm):
+        fn()
+    times = []
+    for i in range(reps):
+        scratch.fill_(float(i))
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    del scratch
+    return [a.elapsed_time(b) * 1e3 for a, b in times]
+
+
+def _warm_times(fn, stream, reps=20, warm=20):
+    """Back-to-back calls on resident inputs (a loop's steady state): `warm`
+    untimed calls, then `reps` calls timed by events.  Returns times (us)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def forward_configs(dn, synth, dev, stream):
+    """The forward-only workloads (2, 3 and 5) and the decode step, each timed
+    warm (back to back on resident inputs) and cold (a 1 GiB eviction before
+    every call; 5 untimed calls, then 20 timed ones, median and minimum), with
+    the fraction of the HBM roofline at its algorithmic bytes."""
+    import torch
+    res = {}
+    med = lambda v: sorted(v)[len(v) // 2]
+
+    def entry(name, nbytes, tokens, warm, cold):
+        floor = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        res[name] = {
+            "bytes": nbytes, "floor_us": round(floor, 2),
+            "warm_us": {"mean": round(sum(warm) / len(warm), 2), "median": round(med(warm), 2),
+                        "min": round(min(warm), 2)},
+            "cold_us": {"median": round(med(cold), 2), "min": round(min(cold), 2)},
+            "frac_warm": round(floor / (sum(warm) / len(warm)), 4),
+            "frac_cold": round(floor / med(cold), 4),
+            "tokens_per_s_cold": round(tokens / (med(cold) * 1e-6), 1),
+        }
+
+    for wid in FWD_WORKLOADS:
+        sh = synth.WORKLOADS[wid]
+        x = synth.workload_inputs(wid)
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+        del x
+        fn = lambda: dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+        warm = _warm_times(fn, stream)
+        cold = _cold_times(fn, stream)
+        entry(synth.WORKLOAD_NAMES[wid], workload_bytes(sh, False), sh.B * sh.T, warm, cold)
+        del d
+        torch.cuda.empty_cache()
+    x = synth.decode_inputs()
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    fn = lambda: dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], d["state"])
+    warm = _warm_times(fn, stream)
+    cold = _cold_times(fn, stream)
+    entry("decode-B256-H32-d128", decode_bytes(), 256, warm, cold)
+    res["how"] = ("warm: 20 untimed then 20 timed back-to-back calls on resident inputs; cold: 5 "
+                  "untimed calls, then 20 timed calls each after a 1 GiB write (median, min); "
+                  "frac = the HBM floor at 8 TB/s of the algorithmic bytes over the time; "
+                  "tokens_per_s_cold counts the decode batch as tokens")
+    return res
 
 
 def measured_peaks(torch, dev, stream):
@@ -485,10 +603,33 @@ def cpu_baseline(x, sh, backward, budget_s, variant="delta"):
             break
         npairs = min(npairs * 4, sh.B * sh.H)
     token_heads = npairs * T
+    # the same oracle on one thread, over one pair of the sample
+    one = {k: (v[:1] if v is not None else None) for k, v in xs.items()}
+    h01 = h0[:1] if h0 is not None else None
+    t0 = time.perf_counter()
+    ofwd(one["q"], one["k"], one["v"], one["beta"], one["g"], h01, nthreads=1)
+    if backward:
+        obwd(one["q"], one["k"], one["v"], one["beta"], one["g"], h01, dO[:1], dhT[:1], nthreads=1)
+    t1 = time.perf_counter() - t0
     return {"value": round(token_heads / sh.H / elapsed, 1), "unit": "tokens/s",
-            "cores": nthr, "kind": "oracle",
-            "sample": "%d (batch, head) pairs x %d tokens (%s), %.1f s; tokens/s counts a token "
-                      "as all %d heads" % (npairs, T, "fwd+bwd" if backward else "fwd", elapsed, sh.H)}
+            "cores": nthr, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "%d (batch, head) pairs x %d tokens (%s), %.1f s on %d threads; tokens/s counts "
+                      "a token as all %d heads" % (npairs, T, "fwd+bwd" if backward else "fwd", elapsed,
+                                                   nthr, sh.H),
+            "one_thread": {"value": round(T / sh.H / t1, 1), "unit": "tokens/s", "seconds": round(t1, 2),
+                           "sample": "1 (batch, head) pair x %d tokens on 1 thread" % T}}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_decode(args, dn, synth, dev):

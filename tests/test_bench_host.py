@@ -12,15 +12,23 @@ import bench  # noqa: E402
 from chunkwise_delta_rule_wy_amd import synth  # noqa: E402
 
 
-def test_chunk_gradient_bytes_per_chunk_head():
+def test_chunk_gradient_bytes_per_token_head():
     # per token and head at dk = 128, dv = 256: q, k, v, dO in bf16, beta and g in
-    # fp32 read; dq, dk, dv, dbeta, dg in fp32 written; per (chunk, head) the bf16
-    # chunk state h and its gradient dh (dk x dv each)
+    # fp32 read; dq, dk, dv, dbeta, dg in fp32 written (3600 B); the bf16 chunk
+    # states the kernel also reads are intermediates, counted apart
     read = 128 * 2 + 128 * 2 + 256 * 2 + 256 * 2 + 4 + 4
     written = 128 * 4 + 128 * 4 + 256 * 4 + 4 + 4
-    per_chunk_head = 64 * (read + written) + 2 * 128 * 256 * 2
-    assert per_chunk_head == 361472
-    assert bench.chunk_grad_bytes(synth.WORKLOADS[4]) == per_chunk_head * 4096
+    assert read + written == 3600
+    assert bench.chunk_grad_bytes(synth.WORKLOADS[4]) == 3600 * 4 * 4096 * 16  # 943.7 MB
+    assert round(bench.chunk_grad_bytes(synth.WORKLOADS[4]) / 1e6, 1) == 943.7
+    assert bench.chunk_state_bytes(synth.WORKLOADS[4]) == 4096 * 2 * 128 * 256 * 2
+
+
+def test_forward_and_decode_floors():
+    # the HBM floors of the forward workloads and the decode step at 8 TB/s
+    floors = {w: bench.workload_bytes(synth.WORKLOADS[w], False) / 8e12 * 1e6 for w in (2, 3, 5)}
+    assert [round(floors[w], 1) for w in (2, 3, 5)] == [34.7, 52.7, 274.7]
+    assert round(bench.decode_bytes() / 8e12 * 1e6, 1) == 135.3
 
 
 def test_forward_bytes():

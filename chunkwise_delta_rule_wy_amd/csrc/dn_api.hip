@@ -35,7 +35,7 @@ dn_status check_shape(const dn_shape *s, const int32_t *cu, bool chunk32 = false
 
 // Upper bound on the number of 64-token chunks over all sequences.
 int64_t max_chunks(const dn_shape *s, bool varlen) {
-  if (!varlen) return (int64_t)s->B * ((s->T + 63) / 64);
+  if (!varlen) return (int64_t)s->B * (((int64_t)s->T + 63) / 64);
   // sum_n ceil(L_n / 64) <= floor(T / 64) + n_seqs
   return (int64_t)s->T / 64 + s->n_seqs;
 }
@@ -74,7 +74,7 @@ dn::FwdParams fwd_params(const dn_shape *s, const void *q, const void *k, const 
   p.H = s->H;
   p.DV = s->Dv;
   p.N = s->n_seqs;
-  p.NC = (s->T + 63) / 64;
+  p.NC = (int)(((int64_t)s->T + 63) / 64);
   p.ntiles = s->Dv / 64;
   p.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
   return p;
@@ -189,7 +189,7 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   bp.H = s->H;
   bp.DV = s->Dv;
   bp.N = s->n_seqs;
-  bp.NC = (s->T + 63) / 64;
+  bp.NC = (int)(((int64_t)s->T + 63) / 64);
   bp.ntiles = s->Dv / 64;
   bp.xcd_map = fp.xcd_map;
   bp.total_chunks = (int)w.nchunks;
@@ -353,7 +353,10 @@ static dn_status rows_check(int32_t B, int32_t T, int32_t H, int32_t Dk, int32_t
   if (B <= 0 || T < 0 || H <= 0) return DN_EINVAL;
   if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
   if (Dk != 64 && Dk != 128) return DN_EUNSUPPORTED;
-  if ((int64_t)B * T * H / 4 >= (int64_t)1 << 31) return DN_EUNSUPPORTED;  // grid size
+  // grid size: B T H / 4 rows of workgroups below 2^31 (B T checked first, so
+  // that the product cannot overflow)
+  const int64_t bt = (int64_t)B * T;
+  if (bt > ((int64_t)1 << 33) / H || bt * H / 4 >= (int64_t)1 << 31) return DN_EUNSUPPORTED;
   return DN_OK;
 }
 

@@ -40,18 +40,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def _compile(src, objdir):
+    obj = os.path.join(objdir, src.replace(".hip", ".o"))
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    cmd = [_hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msg = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
+                    if "not a recognized feature" not in ln)
+    return obj, r.returncode, msg
+
+
 def _link(sources, lib, verbose):
+    from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
+    jobs = max(1, min(len(sources), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1)), 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, objdir), sources))
     objs = []
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    for src in sources:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [_hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        msg = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
-                        if "not a recognized feature" not in ln)
-        if r.returncode != 0:
+    for src, (obj, rc, msg) in zip(sources, results):
+        if rc != 0:
             raise RuntimeError("hipcc failed for %s:\n%s" % (src, msg))
         if verbose and msg.strip():
             print(msg, file=sys.stderr)

@@ -22,7 +22,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "longhorn_eps", "longhorn_eps_bwd", "longhorn_fwd",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_noalloc", "recurrent_step", "longhorn_eps", "longhorn_eps_bwd", "longhorn_fwd",
            "longhorn_bwd", "prologue", "prologue_bwd", "DeltaRule", "delta_rule",
            "load_library", "LIB_PATH", "DnError"]
 
@@ -80,6 +80,8 @@ def load_library():
     lib.dn_chunk_bwd_prologue.restype = ctypes.c_int
     lib.dn_chunk_bwd_longhorn.argtypes = [S] + [P] * 7 + [P, P] + [P] + [P] * 6 + [P, ctypes.c_size_t, P, P]
     lib.dn_chunk_bwd_longhorn.restype = ctypes.c_int
+    lib.dn_chunk_bwd_noalloc.argtypes = [S] + [P] * 7 + [P, P] + [P] * 6 + [P]
+    lib.dn_chunk_bwd_noalloc.restype = ctypes.c_int
     lib.dn_recurrent_step.argtypes = [ctypes.c_int32] * 5 + [P] * 7 + [P]
     lib.dn_recurrent_step.restype = ctypes.c_int
     lib.dn_longhorn_eps.argtypes = [ctypes.c_int32] * 5 + [P] * 3 + [P]
@@ -283,6 +285,42 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
         _ptr(cu_seqlens), _ptr(dO), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),
         _ptr(dg), _ptr(dh0), _ptr(workspace), workspace.numel(), _stream(dev), ev))
     return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dh0=dh0)
+
+
+def chunk_bwd_noalloc(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, out=None):
+    """``chunk_bwd`` (recomputing) through ``dn_chunk_bwd_noalloc``: the
+    library's static scratch buffer replaces the workspace, so the call
+    allocates no device memory of its own.  ``out``: optional dict of
+    preallocated float32 gradients (dq, dk, dv, dbeta, dg, dh0) to write into;
+    missing ones are allocated here.  Returns that dict."""
+    lib = load_library()
+    s, N = _shape(q, v, cu_seqlens, 64)
+    dev = q.device
+    B, T, H, Dk, Dv = s.B, s.T, s.H, s.Dk, s.Dv
+    _need(q, "q", q.dtype, (B, T, H, Dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, Dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, Dv), dev)
+    _need(dO, "dO", q.dtype, (B, T, H, Dv), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(g, "g", torch.float32, (B, T, H), dev)
+    _need(h0, "h0", torch.float32, (N, H, Dk, Dv), dev)
+    _need(dhT, "dhT", torch.float32, (N, H, Dk, Dv), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    shapes = dict(dq=(B, T, H, Dk), dk=(B, T, H, Dk), dv=(B, T, H, Dv), dbeta=(B, T, H), dg=(B, T, H),
+                  dh0=(N, H, Dk, Dv))
+    res = dict(out) if out is not None else {}
+    for name, shp in shapes.items():
+        if name == "dg" and g is None:
+            res[name] = None
+        elif res.get(name) is None:
+            res[name] = torch.empty(shp, dtype=torch.float32, device=dev)
+        else:
+            _need(res[name], name, torch.float32, shp, dev)
+    _check("dn_chunk_bwd_noalloc", lib.dn_chunk_bwd_noalloc(
+        ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(cu_seqlens),
+        _ptr(dO), _ptr(dhT), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dbeta"]),
+        _ptr(res["dg"]), _ptr(res["dh0"]), _stream(dev)))
+    return res
 
 
 def bwd_workspace_bytes(B, T, H, Dk, Dv, n_seqs=None, dtype=torch.bfloat16, chunk=64) -> int:

@@ -16,7 +16,7 @@ PROBE_SOURCES = ["dn_probe.hip"]
 # per-source flags: the probe's MFMA loop keeps its accumulators in VGPRs (with
 # AGPR accumulators the register allocator shuffles them between rounds)
 EXTRA_FLAGS = {"dn_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-SOURCES = ["dn_api.hip", "dn_fwd.hip", "dn_fwd32.hip", "dn_fwd_f32.hip", "dn_bwd.hip", "dn_scan.hip", "dn_bwd_chunk.hip", "dn_step.hip", "dn_longhorn.hip", "dn_prologue.hip", "dn_conv.hip"]
+SOURCES = ["dn_api.hip", "dn_fwd.hip", "dn_fwd32.hip", "dn_fwd_f32.hip", "dn_bwd.hip", "dn_scan.hip", "dn_bwd_chunk.hip", "dn_step.hip", "dn_longhorn.hip", "dn_prologue.hip", "dn_conv.hip", "dn_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -2,6 +2,7 @@
 // Every entry point validates on the host and enqueues nothing on error; it
 // never allocates, frees or synchronises.
 #include "dn.h"
+#include "dn_entry.h"
 #include "dn_internal.h"
 
 namespace {
@@ -124,6 +125,27 @@ dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t
   return DN_OK;
 }
 
+}  // namespace
+
+namespace dn {
+
+dn_status bwd_check(const dn_shape *s, const void *q, const void *k, const void *v, const float *beta,
+                    const float *g, const int32_t *cu_seqlens, const void *dO, const float *dq, const float *dk,
+                    const float *dv, const float *dbeta, const float *dg) {
+  dn_status st = check_train(s, cu_seqlens, q, k, v, beta);
+  if (st != DN_OK) return st;
+  if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
+  if (s->T > 0) {
+    if (!dO || !dq || !dk || !dv || !dbeta) return DN_EINVAL;
+    if (!aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return DN_EINVAL;
+  }
+  return DN_OK;
+}
+
+}  // namespace dn
+
+namespace {
+
 // Raw inputs of the input prologue, or the Longhorn step size's beta, when
 // their backward is folded into the chunk-gradient kernel.
 struct ProIn {
@@ -142,13 +164,8 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
                   const float *dhT, float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
                   void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
                   bool recompute, const ProIn &pro = ProIn()) {
-  dn_status st = check_train(s, cu_seqlens, q, k, v, beta);
+  dn_status st = dn::bwd_check(s, q, k, v, beta, g, cu_seqlens, dO, dq, dk, dv, dbeta, dg);
   if (st != DN_OK) return st;
-  if ((g == nullptr) != (dg == nullptr)) return DN_EINVAL;
-  if (s->T > 0) {
-    if (!dO || !dq || !dk || !dv || !dbeta) return DN_EINVAL;
-    if (!aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return DN_EINVAL;
-  }
   TrainWs w;
   st = train_ws(s, cu_seqlens, workspace, workspace_bytes, stream, w);
   if (st != DN_OK) return st;
@@ -204,6 +221,18 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
 
 }  // namespace
 
+namespace dn {
+
+dn_status bwd_recompute(const dn_shape *s, const void *q, const void *k, const void *v, const float *beta,
+                        const float *g, const float *h0, const int32_t *cu_seqlens, const void *dO,
+                        const float *dhT, float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_run(s, q, k, v, beta, g, h0, cu_seqlens, dO, dhT, dq, dk, dv, dbeta, dg, dh0, workspace,
+                 workspace_bytes, stream, nullptr, true);
+}
+
+}  // namespace dn
+
 extern "C" {
 
 const char *dn_status_str(dn_status s) {
@@ -213,6 +242,8 @@ const char *dn_status_str(dn_status s) {
     case DN_EUNSUPPORTED: return "DN_EUNSUPPORTED: shape or dtype not supported";
     case DN_ENOWS: return "DN_ENOWS: workspace too small";
     case DN_EHIP: return "DN_EHIP: HIP launch error";
+    case DN_ESCRATCH:
+      return "DN_ESCRATCH: the shape needs more than the allocation-free entry point's static scratch buffer";
   }
   return "unknown dn_status";
 }

@@ -59,7 +59,8 @@ typedef enum {
     DN_EINVAL = 1,       /* null required pointer, bad dims, misalignment, g/dg mismatch */
     DN_EUNSUPPORTED = 2, /* valid but not implemented: Dk, Dv, chunk, dtype            */
     DN_ENOWS = 3,        /* workspace smaller than the query function's answer          */
-    DN_EHIP = 4          /* a HIP launch reported an error                              */
+    DN_EHIP = 4,         /* a HIP launch reported an error                              */
+    DN_ESCRATCH = 5      /* dn_chunk_bwd_noalloc: the shape exceeds its static scratch  */
 } dn_status;
 
 typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
@@ -219,6 +220,32 @@ dn_status dn_chunk_bwd_longhorn(const dn_shape *s,
                                 float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t *events);
+
+/*
+ * dn_chunk_bwd_noalloc -- dn_chunk_bwd (the recomputing backward pass, same
+ * kernels, same results bit for bit) for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: its chunk states, state
+ * gradients and packed-sequence chunk table live in a static device buffer
+ * of DN_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends.  The call itself allocates nothing; the
+ * buffer's address on the current device is looked up once, on the first
+ * call on that device.  The shape may need at most that many workspace bytes
+ * (dn_chunk_bwd_workspace(s) <= DN_NOALLOC_SCRATCH_BYTES; B 1, T 2048,
+ * H 16, Dk 128, Dv 128 needs 34.6 MB); a larger one returns DN_ESCRATCH
+ * before anything is enqueued.  Every call on one GPU shares that GPU's buffer:
+ * calls that overlap in time on one GPU (different streams, or different
+ * host threads) race and give wrong results; calls on one stream are
+ * ordered and safe.  Nothing in the buffer needs clearing between calls
+ * (every byte a call reads it first writes).  Arguments, layouts and the
+ * other errors are those of dn_chunk_bwd.
+ */
+#define DN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dn_status dn_chunk_bwd_noalloc(const dn_shape *s,
+    const void *q, const void *k, const void *v, const float *beta, const float *g,
+    const float *h0, const int32_t *cu_seqlens, const void *dO, const float *dhT,
+    float *dq, float *dk, float *dv, float *dbeta, float *dg, float *dh0,
+    hipStream_t stream);
 
 /*
  * One recurrent (decode) step for B x H independent states: the token update

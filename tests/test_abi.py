@@ -13,7 +13,7 @@ import pytest
 import chunkwise_delta_rule_wy_amd as dn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-DN_OK, DN_EINVAL, DN_EUNSUPPORTED, DN_ENOWS, DN_EHIP = range(5)
+DN_OK, DN_EINVAL, DN_EUNSUPPORTED, DN_ENOWS, DN_EHIP, DN_ESCRATCH = range(6)
 
 
 def declared_functions():
@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert lib.dn_status_str(code).decode().startswith("DN_")
 
 
@@ -333,3 +333,23 @@ def test_short_conv_grid_limits(lib):
     assert f(1, 4, 262144, 128, 4, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED
     assert f(1, 4, 262141, 128, 4, 1, 1, P(FAKE), P(FAKE), None, P(FAKE), None) == DN_EUNSUPPORTED
     assert f(1, 4, 262140, 128, 4, 1, 1, None, P(FAKE), None, P(FAKE), None) == DN_EINVAL  # 65535 groups: x checked next
+
+
+def noalloc(lib, s, g=None, dg=None, q=FAKE):
+    P = ctypes.c_void_p
+    return lib.dn_chunk_bwd_noalloc(ctypes.byref(s), P(q), P(FAKE), P(FAKE), P(FAKE), P(g), None, None,
+                                    P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(dg), P(FAKE), None)
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    # argument errors, then the size limit of the static buffer (64 MiB), are
+    # reported before the device is looked up or anything is enqueued
+    assert lib.dn_chunk_bwd_noalloc(None, *([None] * 15), None) == DN_EINVAL
+    assert noalloc(lib, shape(B=0)) == DN_EINVAL
+    assert noalloc(lib, shape(), g=FAKE) == DN_EINVAL          # g without dg
+    assert noalloc(lib, shape(), q=FAKE + 4) == DN_EINVAL      # misaligned
+    assert noalloc(lib, shape(dtype=0)) == DN_EUNSUPPORTED     # bf16 only
+    big = shape(B=4, T=4096, H=16, Dk=128, Dv=256, n_seqs=4)
+    assert lib.dn_chunk_bwd_workspace(ctypes.byref(big)) > 64 << 20
+    assert noalloc(lib, big, g=FAKE, dg=FAKE) == DN_ESCRATCH
+    assert lib.dn_status_str(DN_ESCRATCH).decode().startswith("DN_ESCRATCH")

@@ -17,8 +17,13 @@ from chunkwise_delta_rule_wy_amd import synth
 # rounding errors than a whole tensor's and fluctuates more; its bound is the
 # tensor bound times 2.5.  A chunk whose reference norm is below 1e-6 of its
 # tensor's RMS chunk norm (a gradient that is zero there) is measured
-# absolutely against that RMS instead.
+# absolutely against that RMS instead.  Pairs and chunks of fewer than 64
+# values (a short tail of a per-token scalar such as dbeta or dg) are left to
+# the whole-tensor bound: the relative error of a handful of values is that of
+# single elements, whose rounding is amplified wherever the value is a
+# difference of larger terms.
 CHUNK_FACTOR = 2.5
+MIN_VALUES = 64
 
 
 def _segments(shape_B, T, cu):
@@ -39,15 +44,19 @@ def token_errors(mine, ref, cu=None, chunk=64):
     """Errors of a token tensor ([B, T, H, D] or [B, T, H]) against the oracle.
 
     Returns dict(total, pair [N, H], chunk_max, chunk_at (n, h, c)) where pair
-    is the relative L2 of each (sequence, head) pair and chunk_max the largest
-    relative L2 of any 64-token chunk of any pair."""
+    is the relative L2 of each (sequence, head) pair (0 for a pair of fewer
+    than MIN_VALUES values) and chunk_max the largest relative L2 of any
+    64-token chunk of any pair (of at least MIN_VALUES values)."""
     B, T, H = mine.shape[:3]
     segs = _segments(B, T, cu)
     num = np.zeros((len(segs), H))
     den = np.zeros((len(segs), H))
-    cnum, cden, cidx = [], [], []
+    per_token = int(np.prod(tuple(mine.shape[3:])))
+    small = np.zeros((len(segs), H), dtype=bool)
+    cnum, cden, cidx, csmall = [], [], [], []
     for n, (b, s, e) in enumerate(segs):
         if e == s:
+            small[n] = True
             continue
         x = _as64(mine[b, s:e])
         y = _as64(ref[b, s:e])
@@ -62,18 +71,23 @@ def token_errors(mine, ref, cu=None, chunk=64):
         y2 = np.pad(y2, ((0, pad), (0, 0))).reshape(nc, chunk, H).sum(1)
         num[n] = d2.sum(0)
         den[n] = y2.sum(0)
+        small[n] = L * per_token < MIN_VALUES
         cnum.append(d2)
         cden.append(y2)
         cidx.append(n)
+        tokens = np.minimum(chunk, L - chunk * np.arange(nc))
+        csmall.append(np.repeat((tokens * per_token < MIN_VALUES)[:, None], H, 1))
     total = float(np.sqrt(num.sum() / den.sum())) if den.sum() > 0 else float(np.sqrt(num.sum()))
     with np.errstate(divide="ignore", invalid="ignore"):
         pair = np.where(den > 0, np.sqrt(num / np.where(den > 0, den, 1.0)), np.sqrt(num))
+    pair = np.where(small, 0.0, pair)  # left to the whole-tensor bound
     chunk_max, chunk_at = 0.0, None
     if cnum:
         mean = float(np.mean(np.concatenate([c.ravel() for c in cden])))
         floor = 1e-12 * mean
-        for n, d2, y2 in zip(cidx, cnum, cden):
+        for n, d2, y2, sm in zip(cidx, cnum, cden, csmall):
             r = np.sqrt(d2 / np.where(y2 > floor, y2, max(mean, 1e-300)))
+            r = np.where(sm, 0.0, r)
             i = np.unravel_index(int(np.argmax(r)), r.shape)
             if r[i] > chunk_max:
                 chunk_max, chunk_at = float(r[i]), (n, int(i[1]), int(i[0]))

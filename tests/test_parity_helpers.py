@@ -57,3 +57,24 @@ def test_state_errors_per_pair():
     mine[2, 1] *= 1.1
     e = parity.state_errors(torch.from_numpy(mine), ref)
     assert abs(e["pair"][2, 1] - 0.1) < 1e-12 and e["pair"][0].max() == 0.0
+
+
+def test_blocks_of_few_values_are_left_to_the_tensor_bound():
+    # a per-token scalar: a one-token sequence, and a one-token tail chunk
+    rng = np.random.default_rng(3)
+    lens = (1, 65, 200)
+    cu = np.cumsum((0,) + lens)
+    ref = rng.standard_normal((1, sum(lens), 2))
+    mine = ref.copy()
+    mine[0, 0, 0] *= 1.5          # the one-token sequence
+    mine[0, cu[1] + 64, 1] *= 1.5  # the tail chunk of sequence 1
+    e = parity.token_errors(torch.from_numpy(mine), ref, cu=list(cu))
+    assert e["pair"][0].max() == 0.0
+    assert e["chunk_max"] == 0.0
+    assert e["total"] > 0.0
+    # the same one-token values with 64 values per token are checked
+    ref4 = rng.standard_normal((1, sum(lens), 2, 64))
+    mine4 = ref4.copy()
+    mine4[0, cu[1] + 64, 1] *= 1.5
+    e4 = parity.token_errors(torch.from_numpy(mine4), ref4, cu=list(cu))
+    assert e4["chunk_at"] == (1, 1, 1) and e4["chunk_max"] > 0.4

@@ -166,7 +166,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # the clocks take some 40 steps of steady work to settle after a start
     ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--workload", default="4")
+    ap.add_argument("--workload", default="4",
+                    help="2, 3, 4, 5, 6 (numbered workloads), dec (decode step), conv (short "
+                         "convolution) or chunksize (forward and training pair against the chunk size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--chunk", type=int, choices=(32, 64), default=64,
@@ -213,6 +215,8 @@ def main():
         return bench_decode(args, dn, synth, dev)
     if wid == "conv":
         return bench_conv(args, dn, synth, dev)
+    if wid == "chunksize":
+        return bench_chunk_sizes(args, dn, synth, dev)
     wid = int(wid)
     sh = synth.WORKLOADS[wid]
     backward = sh.backward
@@ -630,6 +634,43 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def bench_chunk_sizes(args, dn, synth, dev):
+    """The chunk-size comparison of the DeltaNet rebuttal (answer Q1: forward
+    and backward time against the chunk size, at sequence length 4096, batch
+    2, head dimension 128, 16 heads), on the ungated delta rule in bf16: the
+    forward pass with 32- and 64-token chunks, and the training pair (the
+    forward pass storing the chunk states, then the backward pass reading
+    them) with 64-token chunks, each timed warm and cold."""
+    import torch
+    sh = synth.Shape(2, 4096, 16, 128, 128, torch.bfloat16, gated=False, has_h0=False, backward=True)
+    x = synth.make_inputs(sh, seed=1301)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    stream = torch.cuda.current_stream(dev)
+    med = lambda v: sorted(v)[len(v) // 2]
+    res = {}
+    for C in (32, 64):
+        fn = lambda: dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, None, chunk=C)
+        warm, cold = _warm_times(fn, stream), _cold_times(fn, stream)
+        res["fwd_C%d" % C] = {"warm_us": round(sum(warm) / len(warm), 2), "cold_median_us": round(med(cold), 2),
+                              "cold_min_us": round(min(cold), 2)}
+    ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv), dtype=torch.uint8, device=dev)
+
+    def train():
+        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, None, save_workspace=ws)
+        dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], None, None, d["dO"], d["dhT"], workspace=ws, saved=True)
+    warm, cold = _warm_times(train, stream), _cold_times(train, stream)
+    res["fwd+bwd_C64"] = {"warm_us": round(sum(warm) / len(warm), 2), "cold_median_us": round(med(cold), 2),
+                          "cold_min_us": round(min(cold), 2)}
+    th = sh.B * sh.T * sh.H
+    res["chunk_state_bytes_C64"] = 2 * (th // 64) * sh.Dk * sh.Dv * 2
+    res["chunk_state_bytes_C32"] = 2 * (th // 32) * sh.Dk * sh.Dv * 2
+    print(json.dumps({"metric": "chunk-size comparison (DeltaNet rebuttal, answer Q1 setting)",
+                      "config": {"workload": "deltanet-B2-T4096-H16-d128-ungated", "dtype": "bf16"},
+                      "results": res, "how": "warm: mean of 20 back-to-back calls; cold: 20 calls each "
+                      "after a 1 GiB write (median, min); chunk_state_bytes: the bf16 states h and dh "
+                      "the training pair stores and reads per chunk size"}), flush=True)
 
 
 def bench_decode(args, dn, synth, dev):

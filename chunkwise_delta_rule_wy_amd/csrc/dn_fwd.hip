@@ -323,6 +323,35 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
     }
   };
   auto full = [&](int cc) { return (cc + 1) * CH <= si.len; };
+  // Full chunks: K (and g, beta) up front, Q and V from the prep's stage hook
+  // (after the gate tables and after the diagonal block), so that the prep
+  // waves do not stall on all of a chunk's direct loads at once (the loads
+  // still land within the step)
+  auto issue_k = [&](int cc) {
+    const uint32_t slot = sbase + (uint32_t)(cc % NBUF) * LY::SLOT;
+    const size_t r0 = row_base + (size_t)cc * CH;
+    const char *kb_ = gk + (r0 * H + h) * (size_t)(DK * 2);
+    const char *sb = reinterpret_cast<const char *>(v == 0 ? p.g : p.beta) + (r0 * H + h) * 4;
+    const bool scal = (v == 1) || (GATED && v == 0);
+    const uint32_t sdst = slot + (v == 0 ? LY::S_G : LY::S_BETA);
+#pragma unroll
+    for (int i = 0; i < LY::DMA_KQ; ++i) dma16s(kb_, koff[i], slot + LY::S_K + 1024 * (v + 4 * i));
+    if (scal) dma4(sb + soff, sdst);
+  };
+  auto issue_q = [&](int cc) {
+    const uint32_t slot = sbase + (uint32_t)(cc % NBUF) * LY::SLOT;
+    const size_t r0 = row_base + (size_t)cc * CH;
+    const char *qb_ = gq + (r0 * H + h) * (size_t)(DK * 2);
+#pragma unroll
+    for (int i = 0; i < LY::DMA_KQ; ++i) dma16s(qb_, koff[i], slot + LY::S_Q + 1024 * (v + 4 * i));
+  };
+  auto issue_v = [&](int cc) {
+    const uint32_t slot = sbase + (uint32_t)(cc % NBUF) * LY::SLOT;
+    const size_t r0 = row_base + (size_t)cc * CH;
+    const char *vb_ = gv + ((r0 * H + h) * (size_t)DV + dv0) * 2;
+#pragma unroll
+    for (int i = 0; i < LY::DMA_V; ++i) dma16s(vb_, voff[i], slot + LY::S_V + 1024 * (v + 4 * i));
+  };
 
   // chain waves: state slice, lane (n, g) holds rows prow(mt, 4g + i) of column `col`
   f32x4 hs[MT];
@@ -357,7 +386,16 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
                                                       col, sdst);
       }
     } else {
-      if (s + 2 < nch) issue(s + 2);
+      const bool spread = WRITE_O && s + 2 < nch && full(s + 2);
+      if (s + 2 < nch) {
+        if (spread) issue_k(s + 2);
+        else issue(s + 2);
+      }
+      const int cn = s + 2;
+      auto hook = [&](int st) {
+        if (spread && st == 0) issue_q(cn);
+        if (spread && st == 1) issue_v(cn);
+      };
       const int c = s + 1;
       if (c < nch) {
         const uint32_t slot = sbase + (uint32_t)(c % NBUF) * LY::SLOT;
@@ -366,16 +404,17 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
         const int L = min(CH, si.len - c * CH);
         const FwdKsw<DK> ksw{lb.frag};
         if (v == 0) prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 0>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
-                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw);
+                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw, hook);
         else if (v == 1) prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 1>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
-                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw);
+                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw, hook);
         else if (v == 2) prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 2>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
-                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw);
+                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw, hook);
         else prep_chunk<DK, GATED, WRITE_O, MODE_FWD, 3>(lb, slot + LY::S_K, slot + LY::S_Q, slot + LY::S_G,
-                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw);
+                                                         slot + LY::S_BETA, ob, priv, L, scale, ksw, hook);
       }
       // K, Q of chunk s + 2 (and everything older) land before the barrier;
       // its V may stay in flight until the next one
+      if (spread && c >= nch) { issue_q(cn); issue_v(cn); }
       if (s + 2 < nch && full(s + 2)) wait_vm<LY::DMA_V>();
       else wait_vm<0>();
     }

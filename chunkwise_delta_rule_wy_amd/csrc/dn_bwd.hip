@@ -32,19 +32,38 @@ namespace dn {
 // --------------------------------------------------------------- chunk table
 // chunk_base[n] is the global index of sequence n's first chunk,
 // chunk_seq[c] the sequence of global chunk c (-1 past the last chunk).
-__global__ void chunk_table_kernel(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
-                                   int max_chunks) {
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int n = 0; n < N; ++n) {
-      chunk_base[n] = acc;
-      acc += (cu[n + 1] - cu[n] + 63) / 64;
-    }
-    chunk_base[N] = acc;
-  }
+// Thread t sums the chunk counts of sequences [t R, (t + 1) R), R = ceil(N /
+// 256); an exclusive scan of the 256 partial sums in LDS gives each thread
+// its first chunk; then every thread fills its sequences' bases and, by
+// binary search, a stripe of chunk_seq.
+constexpr int TABLE_THREADS = 256;
+
+__global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(const int32_t *cu, int N, int32_t *chunk_base,
+                                                                    int32_t *chunk_seq, int max_chunks) {
+  __shared__ int part[TABLE_THREADS];
+  const int t = threadIdx.x;
+  const int per = (N + TABLE_THREADS - 1) / TABLE_THREADS;
+  const int n0 = min(N, t * per), n1 = min(N, n0 + per);
+  int sum = 0;
+  for (int n = n0; n < n1; ++n) sum += (cu[n + 1] - cu[n] + 63) / 64;
+  part[t] = sum;
   __syncthreads();
-  const int total = chunk_base[N];
-  for (int c = threadIdx.x; c < max_chunks; c += blockDim.x) {
+  // Hillis-Steele inclusive scan over the partial sums
+  for (int d = 1; d < TABLE_THREADS; d <<= 1) {
+    const int add = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int acc = part[t] - sum;  // exclusive prefix
+  for (int n = n0; n < n1; ++n) {
+    chunk_base[n] = acc;
+    acc += (cu[n + 1] - cu[n] + 63) / 64;
+  }
+  if (t == TABLE_THREADS - 1) chunk_base[N] = part[TABLE_THREADS - 1];
+  __syncthreads();  // chunk_base (global) complete and visible to the workgroup
+  const int total = part[TABLE_THREADS - 1];
+  for (int c = t; c < max_chunks; c += TABLE_THREADS) {
     int seq = -1;
     if (c < total) {
       int lo = 0, hi = N - 1;  // last n with chunk_base[n] <= c
@@ -61,7 +80,7 @@ __global__ void chunk_table_kernel(const int32_t *cu, int N, int32_t *chunk_base
 
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, stream, cu, N, chunk_base, chunk_seq,
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(TABLE_THREADS), 0, stream, cu, N, chunk_base, chunk_seq,
                      max_chunks);
   return hipGetLastError();
 }

@@ -7,6 +7,7 @@ every (sequence, head) pair, and within 2.5 times that over every 64-token
 chunk of every pair (tests/parity.py).  The full-size workloads are compared
 on every pair, in both backward modes.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -90,6 +91,19 @@ def test_bwd_varlen_xcd_placement(oracle_lib, saved):
     lens = (200, 65, 1, 130)
     sh = Shape(1, sum(lens), 4, 128, 256, torch.bfloat16, True, True, backward=True, lengths=lens)
     check_bwd(make_inputs(sh, seed=43), oracle_lib, "varlen N*H=16", saved)
+
+
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_bwd_varlen_many_sequences(oracle_lib, saved):
+    """600 packed sequences of 0-90 tokens (more sequences than the chunk
+    table's 256 threads, so each thread sums several), d_k = d_v = 64."""
+    rng = np.random.default_rng(600)
+    lens = tuple(int(x) for x in rng.integers(0, 91, size=600))
+    sh = Shape(1, sum(lens), 2, 64, 64, torch.bfloat16, True, True, backward=True, lengths=lens)
+    x = make_inputs(sh, seed=47)
+    gr = check_bwd(x, oracle_lib, "600 sequences", saved)
+    empty = [i for i, L in enumerate(lens) if L == 0]
+    assert empty and all(torch.equal(gr["dh0"][i], x["dhT"][i]) for i in empty)
 
 
 def test_bwd_no_final_state_gradient(oracle_lib):

@@ -449,7 +449,12 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
       for (int k = 0; k < 4; ++k) x[k] -= a[k] * xj;
     }
     float bc = 1.f;
-    if constexpr (!BWD) bc = (16 * PW + c < L) ? ld<float>(baddr + 4 * (16 * PW + c)) : 0.f;
+    if constexpr (!BWD) {
+      // read unconditionally (rows past the end hold stale values) and select:
+      // no branch around the load, so no address register live across it
+      const float bv = ld<float>(baddr + 64 * PW + 4 * c);
+      bc = (16 * PW + c < L) ? bv : 0.f;
+    }
     bf16x4 tv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) tv[k] = (__bf16)(x[k] * bc);

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import chunkwise_delta_rule_wy_amd as dn
+import parity
 from chunkwise_delta_rule_wy_amd import synth
 from chunkwise_delta_rule_wy_amd.synth import Shape, make_inputs, rel_l2
 
@@ -136,15 +137,34 @@ def test_bwd_prologue_fused_matches_composed(oracle_lib, cfg):
         assert e <= TOL, (name, e)
 
 
+_FULL = {}
+
+
+def _full_reference(oracle_lib):
+    """The oracle's composition (prologue, forward, backward, prologue
+    backward) on the whole benchmark step, computed once."""
+    if "ref" not in _FULL:
+        x = synth.workload_inputs(4, raw=True)
+        c = x["gate_scale"]
+        rq, rk, rb, rg = oracle_lib.prologue(x["q_in"], x["k_in"], x["b_in"], x["x_in"], c)
+        ro, _ = oracle_lib.fwd(rq, rk, x["v"], rb, rg, x["h0"])
+        rgr = oracle_lib.bwd(rq, rk, x["v"], rb, rg, x["h0"], x["dO"], x["dhT"])
+        rin = oracle_lib.prologue_bwd(x["q_in"], x["k_in"], x["b_in"], x["x_in"], c,
+                                      rgr["dq"], rgr["dk"], rgr["dbeta"], rgr["dg"])
+        _FULL["ref"] = (x, ro, rgr, rin)
+    return _FULL["ref"]
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("fused", [False, True], ids=["composed", "fused"])
-def test_prologue_composed_full_size_sampled(oracle_lib, fused):
+def test_prologue_composed_full_size_every_pair(oracle_lib, fused):
     """The benchmark's step with the prologue (B=4 T=4096 H=16 dk=128 dv=256):
     prologue, forward, backward and prologue backward on the GPU (composed from
     the separate passes, or with the prologue's backward folded into the
     chunk-gradient kernel after the state-saving forward pass) against the
-    oracle's composition, on two (batch, head) pairs."""
+    oracle's composition, on every (batch, head) pair and every chunk."""
     sh = synth.WORKLOADS[4]
-    x = synth.workload_inputs(4, raw=True)
+    x, ro, rgr, rin = _full_reference(oracle_lib)
     d = to_dev(x)
     c = x["gate_scale"]
     q, k, beta, g = dn.prologue(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c)
@@ -160,23 +180,9 @@ def test_prologue_composed_full_size_sampled(oracle_lib, fused):
         din = dn.prologue_bwd(d["q_in"], d["k_in"], d["b_in"], d["x_in"], c, gr["dq"], gr["dk"],
                               gr["dbeta"], gr["dg"])
     torch.cuda.synchronize()
-    o = o.cpu()
-    din = [t.cpu() for t in din]
-    dv, dh0 = gr["dv"].cpu(), gr["dh0"].cpu()
-    rng = np.random.default_rng(8)
-    for idx in rng.choice(sh.B * sh.H, size=2, replace=False):
-        b, h = int(idx) // sh.H, int(idx) % sh.H
-        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
-        st = lambda t: t[b:b + 1, h:h + 1].contiguous()
-        rq, rk, rb, rg = oracle_lib.prologue(sl(x["q_in"]), sl(x["k_in"]), sl(x["b_in"]), sl(x["x_in"]), c)
-        ro, _ = oracle_lib.fwd(rq, rk, sl(x["v"]), rb, rg, st(x["h0"]))
-        rgr = oracle_lib.bwd(rq, rk, sl(x["v"]), rb, rg, st(x["h0"]), sl(x["dO"]), st(x["dhT"]))
-        rin = oracle_lib.prologue_bwd(sl(x["q_in"]), sl(x["k_in"]), sl(x["b_in"]), sl(x["x_in"]), c,
-                                      rgr["dq"], rgr["dk"], rgr["dbeta"], rgr["dg"])
-        errs = {"o": rel_l2(sl(o), ro), "dv": rel_l2(sl(dv), rgr["dv"]), "dh0": rel_l2(st(dh0), rgr["dh0"])}
-        for name, mine, r in zip(("dq_in", "dk_in", "db_in", "dx_in"), din, rin):
-            errs[name] = rel_l2(sl(mine), r)
-        print("prologue workload 4 pair (%d,%d)" % (b, h), " ".join("%s %.2e" % kv for kv in errs.items()),
-              flush=True)
-        for name, e in errs.items():
-            assert e <= TOL, (name, e)
+    label = "prologue %s workload 4" % ("fused" if fused else "composed")
+    parity.check("o", parity.token_errors(o.cpu(), ro), TOL, label)
+    parity.check("dv", parity.token_errors(gr["dv"].cpu(), rgr["dv"]), TOL, label)
+    parity.check("dh0", parity.state_errors(gr["dh0"].cpu(), rgr["dh0"]), TOL, label)
+    for name, mine, r in zip(("dq_in", "dk_in", "db_in", "dx_in"), din, rin):
+        parity.check(name, parity.token_errors(mine.cpu(), r), TOL, label)

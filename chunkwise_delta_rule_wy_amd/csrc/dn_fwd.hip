@@ -323,10 +323,12 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
     }
   };
   auto full = [&](int cc) { return (cc + 1) * CH <= si.len; };
-  // Full chunks: K (and g, beta) up front, Q and V from the prep's stage hook
-  // (after the gate tables and after the diagonal block), so that the prep
-  // waves do not stall on all of a chunk's direct loads at once (the loads
-  // still land within the step)
+  // Full chunks of the plain forward: K (and g, beta) up front, Q and V from
+  // the prep's stage hook (after the gate tables and after the diagonal
+  // block), so that the prep waves do not stall on all of a chunk's direct
+  // loads at once (the loads still land within the step).  The state-storing
+  // variant issues everything up front: with its state stores in the same
+  // step, the later loads measured slower.
   auto issue_k = [&](int cc) {
     const uint32_t slot = sbase + (uint32_t)(cc % NBUF) * LY::SLOT;
     const size_t r0 = row_base + (size_t)cc * CH;
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_bf16_kernel(FwdParams p) {
                                                       col, sdst);
       }
     } else {
-      const bool spread = WRITE_O && s + 2 < nch && full(s + 2);
+      const bool spread = WRITE_O && !STORE_STATES && s + 2 < nch && full(s + 2);
       if (s + 2 < nch) {
         if (spread) issue_k(s + 2);
         else issue(s + 2);

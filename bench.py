@@ -422,14 +422,33 @@ def main():
 FWD_WORKLOADS = (2, 3, 5)
 
 
-def _cold_times(fn, stream, reps=20, warm=5):
-    """The cold protocol: `warm` untimed calls, then `reps` calls, each after a
-    1 GiB write that evicts the L2s and the 256 MB Infinity Cache, timed by
-    events on the launch stream.  Returns the list of times (us)."""
+WARM_MS = 60.0
+
+
+def _settle(fn, stream, warm_ms=WARM_MS):
+    """Untimed calls for about `warm_ms` of device time (at least 20): the
+    shader clock takes tens of milliseconds of steady work to settle after the
+    GPU has idled, e.g. while the host built the next workload's inputs."""
+    import torch
+    e0, e1 = TimingEvent(), TimingEvent()
+    e0.record(stream)
+    for _ in range(5):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_call_ms = max(e0.elapsed_time(e1) / 5, 1e-3)
+    for _ in range(min(5000, max(20, int(warm_ms / per_call_ms) + 1))):
+        fn()
+
+
+def _cold_times(fn, stream, reps=20):
+    """The cold protocol: untimed calls until the clocks settle, then `reps`
+    calls, each after a 1 GiB write that evicts the L2s and the 256 MB
+    Infinity Cache, timed by events on the launch stream.  Returns the list of
+    times (us)."""
     import torch
     scratch = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=torch.device("cuda:0"))
-    for _ in range(warm):
-        fn()
+    _settle(fn, stream)
     times = []
     for i in range(reps):
         scratch.fill_(float(i))
@@ -443,12 +462,12 @@ def _cold_times(fn, stream, reps=20, warm=5):
     return [a.elapsed_time(b) * 1e3 for a, b in times]
 
 
-def _warm_times(fn, stream, reps=20, warm=20):
-    """Back-to-back calls on resident inputs (a loop's steady state): `warm`
-    untimed calls, then `reps` calls timed by events.  Returns times (us)."""
+def _warm_times(fn, stream, reps=20):
+    """Back-to-back calls on resident inputs (a loop's steady state): untimed
+    calls until the clocks settle, then `reps` calls timed by events.  Returns
+    times (us)."""
     import torch
-    for _ in range(warm):
-        fn()
+    _settle(fn, stream)
     ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
     for a, b in ev:
         a.record(stream)
@@ -461,7 +480,7 @@ def _warm_times(fn, stream, reps=20, warm=20):
 def forward_configs(dn, synth, dev, stream):
     """The forward-only workloads (2, 3 and 5) and the decode step, each timed
     warm (back to back on resident inputs) and cold (a 1 GiB eviction before
-    every call; 5 untimed calls, then 20 timed ones, median and minimum), with
+    every call; 20 timed calls, median and minimum), with
     the fraction of the HBM roofline at its algorithmic bytes."""
     import torch
     res = {}
@@ -496,8 +515,9 @@ def forward_configs(dn, synth, dev, stream):
     warm = _warm_times(fn, stream)
     cold = _cold_times(fn, stream)
     entry("decode-B256-H32-d128", decode_bytes(), 256, warm, cold)
-    res["how"] = ("warm: 20 untimed then 20 timed back-to-back calls on resident inputs; cold: 5 "
-                  "untimed calls, then 20 timed calls each after a 1 GiB write (median, min); "
+    res["how"] = ("warm: untimed calls for %.0f ms of device time (at least 20), then 20 timed "
+                  "back-to-back calls on resident inputs; cold: the same untimed calls, then 20 "
+                  "timed calls each after a 1 GiB write (median, min); " % WARM_MS +
                   "frac = the HBM floor at 8 TB/s of the algorithmic bytes over the time; "
                   "tokens_per_s_cold counts the decode batch as tokens")
     return res

@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -68,23 +70,47 @@ __device__ __forceinline__ f32x4 mma16(f32x4 c, f32x4 a, f32x4 b) {
 template <typename E> __device__ __forceinline__ E to_e(float x) { return (E)x; }
 template <typename E> __device__ __forceinline__ float to_f(E x) { return (float)x; }
 
+// Two fp32 to two bf16 (round to nearest even) in one 32-bit word.  Packing
+// through 32-bit words makes the compiler emit one v_cvt_pk_bf16_f32 per pair
+// also where the result feeds an MFMA operand (element-wise bf16 vectors are
+// converted one value at a time there and then merged with v_perm_b32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2v));
+}
+__device__ __forceinline__ bf16x4 cvt_bf16x4(const f32x4 &v) {
+  return __builtin_bit_cast(bf16x4, (u32x2){pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])});
+}
+
 // B fragment (32-index block) from two stacked accumulator tiles
 template <typename E>
 __device__ __forceinline__ F32<E> bfrag(const f32x4 &lo, const f32x4 &hi) {
-  F32<E> r;
+  if constexpr (std::is_same<E, bf16>::value) {
+    return __builtin_bit_cast(bf16x8, (u32x4){pk_bf16(lo[0], lo[1]), pk_bf16(lo[2], lo[3]), pk_bf16(hi[0], hi[1]),
+                                              pk_bf16(hi[2], hi[3])});
+  } else {
+    F32<E> r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = to_e<E>(lo[i]);
-    r[4 + i] = to_e<E>(hi[i]);
+    for (int i = 0; i < 4; ++i) {
+      r[i] = to_e<E>(lo[i]);
+      r[4 + i] = to_e<E>(hi[i]);
+    }
+    return r;
   }
-  return r;
 }
 template <typename E>
 __device__ __forceinline__ F16<E> bfrag16(const f32x4 &t) {
-  F16<E> r;
+  if constexpr (std::is_same<E, bf16>::value) {
+    return cvt_bf16x4(t);
+  } else {
+    F16<E> r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = to_e<E>(t[i]);
-  return r;
+    for (int i = 0; i < 4; ++i) r[i] = to_e<E>(t[i]);
+    return r;
+  }
 }
 
 // Four consecutive E values from LDS (8-byte aligned for bf16, 16 for f32)

@@ -63,12 +63,7 @@ __device__ __forceinline__ void dma16s(const void *base, uint32_t voff, uint32_t
 }
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
-__device__ __forceinline__ bf16x4 cvt4(const f32x4 &v) {
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (__bf16)v[i];
-  return r;
-}
+__device__ __forceinline__ bf16x4 cvt4(const f32x4 &v) { return cvt_bf16x4(v); }
 __device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }

@@ -11,7 +11,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t esize(int dtype) { return dtype == DN_BF16 ? 2 : 4; }
 
-// chunk32: the forward pass also takes 32-token chunks (bf16 inputs)
+// chunk32: the pass also takes 32-token chunks (bf16 inputs)
 dn_status check_shape(const dn_shape *s, const int32_t *cu, bool chunk32 = false) {
   if (!s) return DN_EINVAL;
   if (s->B <= 0 || s->T < 0 || s->H <= 0 || s->Dk <= 0 || s->Dv <= 0 || s->n_seqs <= 0)
@@ -34,11 +34,15 @@ dn_status check_shape(const dn_shape *s, const int32_t *cu, bool chunk32 = false
   return DN_OK;
 }
 
-// Upper bound on the number of 64-token chunks over all sequences.
+// Chunk length of a shape that passed check_shape (64 or 32).
+int chunk_len(const dn_shape *s) { return s->chunk == 32 ? 32 : 64; }
+
+// Upper bound on the number of chunks over all sequences.
 int64_t max_chunks(const dn_shape *s, bool varlen) {
-  if (!varlen) return (int64_t)s->B * (((int64_t)s->T + 63) / 64);
-  // sum_n ceil(L_n / 64) <= floor(T / 64) + n_seqs
-  return (int64_t)s->T / 64 + s->n_seqs;
+  const int C = chunk_len(s);
+  if (!varlen) return (int64_t)s->B * (((int64_t)s->T + C - 1) / C);
+  // sum_n ceil(L_n / C) <= floor(T / C) + n_seqs
+  return (int64_t)s->T / C + s->n_seqs;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -75,7 +79,7 @@ dn::FwdParams fwd_params(const dn_shape *s, const void *q, const void *k, const 
   p.H = s->H;
   p.DV = s->Dv;
   p.N = s->n_seqs;
-  p.NC = (int)(((int64_t)s->T + 63) / 64);
+  p.NC = (int)(((int64_t)s->T + chunk_len(s) - 1) / chunk_len(s));
   p.ntiles = s->Dv / 64;
   p.xcd_map = ((s->n_seqs * s->H) % 8) == 0;
   return p;
@@ -84,7 +88,7 @@ dn::FwdParams fwd_params(const dn_shape *s, const void *q, const void *k, const 
 // Checks shared by the passes that use the backward workspace (bf16 only).
 dn_status check_train(const dn_shape *s, const int32_t *cu, const void *q, const void *k, const void *v,
                       const float *beta) {
-  dn_status st = check_shape(s, cu);
+  dn_status st = check_shape(s, cu, true);
   if (st != DN_OK) return st;
   if (s->dtype != DN_BF16) return DN_EUNSUPPORTED;  // the backward kernels are bf16
   if (s->T > 0) {
@@ -117,7 +121,8 @@ dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t
   if (varlen) {
     w.chunk_base = reinterpret_cast<int32_t *>(ws + L.table);
     w.chunk_seq = w.chunk_base + s->n_seqs + 1;
-    hipError_t e = dn::launch_chunk_table(cu, s->n_seqs, w.chunk_base, w.chunk_seq, (int)w.nchunks, stream);
+    hipError_t e = dn::launch_chunk_table(cu, s->n_seqs, w.chunk_base, w.chunk_seq, (int)w.nchunks, chunk_len(s),
+                                          stream);
     if (e != hipSuccess) return DN_EHIP;
   }
   w.states = reinterpret_cast<bf16 *>(ws + L.states);
@@ -176,7 +181,8 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   fp.states = w.states;
   fp.chunk_base = w.chunk_base;
   if (recompute) {
-    hipError_t e = dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
+    hipError_t e = s->chunk == 32 ? dn::launch_fwd_c32(fp, s->Dk, true, false, stream)
+                                  : dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
     if (e != hipSuccess) return DN_EHIP;
   }
   if (events && events[1] && hipEventRecord(events[1], stream) != hipSuccess) return DN_EHIP;
@@ -206,10 +212,11 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   bp.H = s->H;
   bp.DV = s->Dv;
   bp.N = s->n_seqs;
-  bp.NC = (int)(((int64_t)s->T + 63) / 64);
+  bp.NC = fp.NC;
   bp.ntiles = s->Dv / 64;
   bp.xcd_map = fp.xcd_map;
   bp.total_chunks = (int)w.nchunks;
+  bp.chunk = chunk_len(s);
   bp.q_in = pro.q_in;
   bp.k_in = pro.k_in;
   bp.x_in = pro.x_in;
@@ -268,7 +275,7 @@ dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const vo
   dn::FwdParams p = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
   p.o = o;
   p.hT = hT;
-  if (s->chunk == 32) return from_hip(dn::launch_fwd_c32(p, s->Dk, stream));
+  if (s->chunk == 32) return from_hip(dn::launch_fwd_c32(p, s->Dk, false, true, stream));
   return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, false, true, stream));
 }
 
@@ -312,6 +319,7 @@ dn_status dn_chunk_fwd_save(const dn_shape *s, const void *q, const void *k, con
   p.hT = hT;
   p.states = w.states;
   p.chunk_base = w.chunk_base;
+  if (s->chunk == 32) return from_hip(dn::launch_fwd_c32(p, s->Dk, true, true, stream));
   return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, true, true, stream));
 }
 
@@ -332,6 +340,7 @@ dn_status dn_chunk_bwd_prologue(const dn_shape *s, const void *q, const void *k,
                                 float *dh0, void *workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t *events) {
   if ((x_in == nullptr) != (g == nullptr)) return DN_EINVAL;
+  if (s && s->chunk == 32) return DN_EUNSUPPORTED;  // the folded variants take 64-token chunks
   if (s && s->T > 0) {
     if (!q_in || !k_in || !aligned16(q_in) || !aligned16(k_in)) return DN_EINVAL;
   }
@@ -350,6 +359,7 @@ dn_status dn_chunk_bwd_longhorn(const dn_shape *s, const void *q, const void *k,
                                 const float *beta, float *dq, float *dk, float *dv, float *dbeta, float *dg,
                                 float *dh0, void *workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t *events) {
+  if (s && s->chunk == 32) return DN_EUNSUPPORTED;  // the folded variants take 64-token chunks
   if (s && s->T > 0 && !beta) return DN_EINVAL;
   ProIn pro;
   pro.beta_raw = beta ? beta : eps;  // T == 0: nothing is read, but the variant is still the folded one

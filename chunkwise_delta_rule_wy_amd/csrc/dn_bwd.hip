@@ -30,7 +30,7 @@
 namespace dn {
 
 // --------------------------------------------------------------- chunk table
-// chunk_base[n] is the global index of sequence n's first chunk,
+// chunk_base[n] is the global index of sequence n's first chunk of C tokens,
 // chunk_seq[c] the sequence of global chunk c (-1 past the last chunk).
 // Thread t sums the chunk counts of sequences [t R, (t + 1) R), R = ceil(N /
 // 256); an exclusive scan of the 256 partial sums in LDS gives each thread
@@ -39,13 +39,13 @@ namespace dn {
 constexpr int TABLE_THREADS = 256;
 
 __global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(const int32_t *cu, int N, int32_t *chunk_base,
-                                                                    int32_t *chunk_seq, int max_chunks) {
+                                                                    int32_t *chunk_seq, int max_chunks, int C) {
   __shared__ int part[TABLE_THREADS];
   const int t = threadIdx.x;
   const int per = (N + TABLE_THREADS - 1) / TABLE_THREADS;
   const int n0 = min(N, t * per), n1 = min(N, n0 + per);
   int sum = 0;
-  for (int n = n0; n < n1; ++n) sum += (cu[n + 1] - cu[n] + 63) / 64;
+  for (int n = n0; n < n1; ++n) sum += (cu[n + 1] - cu[n] + C - 1) / C;
   part[t] = sum;
   __syncthreads();
   // Hillis-Steele inclusive scan over the partial sums
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(const int32_
   int acc = part[t] - sum;  // exclusive prefix
   for (int n = n0; n < n1; ++n) {
     chunk_base[n] = acc;
-    acc += (cu[n + 1] - cu[n] + 63) / 64;
+    acc += (cu[n + 1] - cu[n] + C - 1) / C;
   }
   if (t == TABLE_THREADS - 1) chunk_base[N] = part[TABLE_THREADS - 1];
   __syncthreads();  // chunk_base (global) complete and visible to the workgroup
@@ -79,9 +79,9 @@ __global__ __launch_bounds__(TABLE_THREADS) void chunk_table_kernel(const int32_
 }
 
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
-                              int max_chunks, hipStream_t stream) {
+                              int max_chunks, int chunk, hipStream_t stream) {
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(TABLE_THREADS), 0, stream, cu, N, chunk_base, chunk_seq,
-                     max_chunks);
+                     max_chunks, chunk);
   return hipGetLastError();
 }
 

@@ -120,12 +120,18 @@ struct BwdKsw {
 // -2 eps^2 deps k, the step size's dependence on the key).
 enum : int { EPI_PLAIN = 0, EPI_PRO = 1, EPI_LH = 2 };
 
-template <int DK, bool GATED, int EPI>
+template <int DK, bool GATED, int EPI, int NB>
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   constexpr bool PRO = EPI == EPI_PRO, LH = EPI == EPI_LH;
   using LY = BLay<DK>;
   using RS = Res<MODE_CHUNK>;
   constexpr int KB = LY::KB, MT = LY::MT, RB = LY::RB;
+  // NB 16-token blocks per chunk: 4 (64-token chunks) or 2 (32-token chunks,
+  // which use the first half of every token-indexed buffer and leave every
+  // block with an index >= NB out)
+  static_assert(NB == 4 || NB == 2, "64- or 32-token chunks");
+  constexpr int CHN = 16 * NB;  // tokens per chunk
+  constexpr int NKB = NB / 2;   // 32-token contraction blocks
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const uint32_t sb = (uint32_t)(uintptr_t)(lds_ptr<unsigned char>)smem_raw;
 
@@ -141,11 +147,11 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     if (n_seq >= p.N) return;
   }
   const SeqInfo si = seq_info(p.cu, n_seq, p.T);
-  if (c * CH >= si.len) return;
-  const int L = min(CH, si.len - c * CH);
-  const bool full = L == CH;
+  if (c * CHN >= si.len) return;
+  const int L = min(CHN, si.len - c * CHN);
+  const bool full = L == CHN;
   const int H = p.H, DV = p.DV, ntiles = p.DV / TC;
-  const size_t row0 = (size_t)si.b * p.T + si.t0 + (size_t)c * CH;  // global row of the chunk start
+  const size_t row0 = (size_t)si.b * p.T + si.t0 + (size_t)c * CHN;  // global row of the chunk start
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id(), n = l & 15, g = l >> 4, e4 = (l >> 2) & 3, q4 = l & 3;
 
@@ -213,6 +219,14 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     }
   }
   const bool vrow = (64 * rw + l) / 4 < L;
+  // loads per tile of this row wave in a full chunk: V, dO and its share of S,
+  // dS; with 32-token chunks the waves of rows 32 .. 63 load S and dS only
+  const bool vwave = NB == 4 || rw < NB;
+  auto wait_tiles = [&](auto n_c) {  // at most n tiles of this wave's loads outstanding
+    constexpr int NT = decltype(n_c)::value;
+    if (vwave) wait_vm<NT * LY::DMA_T>();
+    else wait_vm<NT * 2 * LY::DMA_S>();
+  };
   auto issue_tile = [&](int j) {  // row waves: 64 lanes x DMA_T units of 16 bytes each
     const uint32_t tb = tbuf(j);
     const int dv0 = TC * j;
@@ -249,8 +263,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     if (ntiles > 1) issue_tile(1);
     // K, Q, g, beta land before the prep; the tiles stay in flight through it
     if (!full) wait_vm<0>();
-    else if (ntiles > 1) wait_vm<2 * LY::DMA_T>();
-    else wait_vm<LY::DMA_T>();
+    else if (ntiles > 1) wait_tiles(I2{});
+    else wait_tiles(I1{});
   } else {
     wait_vm<0>();
   }
@@ -263,10 +277,10 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     const BwdKsw<DK> ksw{lb_frag};
     const uint32_t priv = sb + LY::O_X + w * PRIV_BYTES;
     const uint32_t kba = sb + LY::O_K, qba = sb + LY::O_Q, ga = sb + LY::O_XG, ba = sb + LY::O_XB;
-    if (w == 0) prep_chunk<DK, GATED, true, MODE_CHUNK, 0>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
-    else if (w == 1) prep_chunk<DK, GATED, true, MODE_CHUNK, 1>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
-    else if (w == 2) prep_chunk<DK, GATED, true, MODE_CHUNK, 2>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
-    else prep_chunk<DK, GATED, true, MODE_CHUNK, 3>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    if (w == 0) prep_chunk<DK, GATED, true, MODE_CHUNK, 0, NB>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    else if (w == 1) prep_chunk<DK, GATED, true, MODE_CHUNK, 1, NB>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    else if (w == 2) prep_chunk<DK, GATED, true, MODE_CHUNK, 2, NB>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
+    else prep_chunk<DK, GATED, true, MODE_CHUNK, 3, NB>(lb, kba, qba, ga, ba, ob, priv, L, dummy, ksw);
   }
   __syncthreads();
 
@@ -281,10 +295,10 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   static_assert(6 * 512 <= LY::ST, "R blocks fit in a state tile");
   auto rcol = [&](auto j_c) {  // straight-line per block column (MFMA results read without branches)
     constexpr int J = decltype(j_c)::value;
-    bf16x4 rc[4];  // R_mJ as B operands (lane (n, g): rows 4g .. 4g + 3 of column n)
+    bf16x4 rc[NB];  // R_mJ as B operands (lane (n, g): rows 4g .. 4g + 3 of column n)
     rc[J] = ld<bf16x4>(ob + RS::O_TT + 512 * J + lb_m);
 #pragma unroll
-    for (int i = J + 1; i < 4; ++i) {
+    for (int i = J + 1; i < NB; ++i) {
       f32x4 z = zero4();
 #pragma unroll
       for (int m = J; m < i; ++m) z = mma16(z, ld<bf16x4>(ob + RS::O_M + 512 * m_block(i, m) + lb_m), rc[m]);
@@ -295,11 +309,13 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     mfma_settle();
   };
   if (w == 4) rcol(I0{});
-  else if (w == 5) rcol(I1{});
-  else if (w == 6) rcol(I2{});
+  else if constexpr (NB == 4) {
+    if (w == 5) rcol(I1{});
+    else if (w == 6) rcol(I2{});
+  }
   // tile 0 lands before the pipeline starts; tile 1 may stay in flight
   if (w >= 4) {
-    if (full && ntiles > 1) wait_vm<LY::DMA_T>();
+    if (full && ntiles > 1) wait_tiles(I1{});
     else wait_vm<0>();
   }
   __syncthreads();
@@ -309,18 +325,18 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   if (w < 4) {
     // =========================== column waves ===========================
     const int cs = w >> 1;  // column set: tile columns 16cs .. 16cs + 15
-    bf16x8 kf[4][KB];       // K fragments, rows 16t + n
+    bf16x8 kf[NB][KB];      // K fragments, rows 16t + n
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kf[t][kb] = ld<bf16x8>(sb + LY::O_K + (lb_frag ^ (64 * kb)) + 16 * t * RB);
+      for (int t = 0; t < NB; ++t) kf[t][kb] = ld<bf16x8>(sb + LY::O_K + (lb_frag ^ (64 * kb)) + 16 * t * RB);
     const uint32_t sfrag = (16 * cs) * RB;  // S / dS rows of the column set
 
     if ((w & 1) == 0) {
       // ------------------------------ F ------------------------------
-      bf16x4 ra[10];  // R_im, m <= i, as A operands (transposed reads of the stored R^T blocks)
+      bf16x4 ra[NB * (NB + 1) / 2];  // R_im, m <= i, as A operands (transposed reads of the stored R^T blocks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int m = 0; m <= i; ++m)
           ra[i * (i + 1) / 2 + m] = ld_tr((m == i ? ob + RS::O_TT + 512 * i : rbuf + 512 * m_block(i, m)) + lb_btr);
@@ -332,14 +348,14 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         // V' writes, lane (n, g): row 16i + n, columns 16cs + 4g .. + 3 at 1024 i + lb_xw
         lb_xw = n * 64 + 16 * ((2 * cs + (g >> 1)) ^ swz_xn(n)) + 8 * (g & 1);
       }
-      f32x4 xp[4], xy[4];  // X of the previous tile; rowsum(X * Y) partials (rows 16i + 4g + e)
+      f32x4 xp[NB], xy[NB];  // X of the previous tile; rowsum(X * Y) partials (rows 16i + 4g + e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xp[i] = xy[i] = zero4();
+      for (int i = 0; i < NB; ++i) xp[i] = xy[i] = zero4();
       for (int s = 0; s <= ntiles; ++s) {
         if (s > 0) {  // rowsum(X * Y) of tile s - 1 (Y handed over by the B wave)
           const uint32_t yb = xbuf(s - 1) + 4096;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < NB; ++i) {
             const bf16x4 yv = ld_tr(yb + 1024 * i + lb_ytr);
 #pragma unroll
             for (int e = 0; e < 4; ++e) xy[i][e] += xp[i][e] * bf2f(yv[e]);
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) hb[kb] = ld<bf16x8>(tb + LY::T_S + sfrag + (lb_frag ^ (64 * kb)));
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < NB; ++t) {
             f32x4 yk = zero4();
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) yk = mma32(yk, kf[t][kb], hb[kb]);
@@ -362,12 +378,12 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           }
           // V' = R diag(beta) X, as V'_i^T = sum_{m<=i} (beta_m X_m)^T R_im^T so
           // that lane (n, g) holds columns 4g .. 4g + 3 of token 16i + n
-          bf16x4 bx[4];
+          bf16x4 bx[NB];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) bx[m] = cvt4(xp[m] * bet4(m));
+          for (int m = 0; m < NB; ++m) bx[m] = cvt4(xp[m] * bet4(m));
           const uint32_t xv = xbuf(s);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < NB; ++i) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int m = 0; m <= i; ++m) acc = mma16(acc, bx[m], ra[i * (i + 1) / 2 + m]);
@@ -379,7 +395,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       }
       // rowsum(X * Y) of this wave's columns
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float sm = row_sum16(xy[i][e]);
@@ -388,15 +404,17 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     } else {
       // ------------------------------ B ------------------------------
       bf16x8 ptf[6];        // P^T fragments (t, kb >= t / 2): (0,0) (0,1) (1,0) (1,1) (2,1) (3,1)
-      bf16x4 rb[10];  // (R_mi)^T, m >= i, as A operands (rows of the stored R^T blocks), index m(m+1)/2 + i
+      bf16x4 rb[NB * (NB + 1) / 2];  // (R_mi)^T, m >= i, as A operands (rows of the stored R^T blocks), index m(m+1)/2 + i
       ptf[0] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 0, l));
-      ptf[1] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 1, l));
       ptf[2] = ld<bf16x8>(ob + RS::O_P + pt_frag(1, 0, l));
-      ptf[3] = ld<bf16x8>(ob + RS::O_P + pt_frag(1, 1, l));
-      ptf[4] = ld<bf16x8>(ob + RS::O_P + pt_frag(2, 1, l));
-      ptf[5] = ld<bf16x8>(ob + RS::O_P + pt_frag(3, 1, l));
+      if constexpr (NB == 4) {
+        ptf[1] = ld<bf16x8>(ob + RS::O_P + pt_frag(0, 1, l));
+        ptf[3] = ld<bf16x8>(ob + RS::O_P + pt_frag(1, 1, l));
+        ptf[4] = ld<bf16x8>(ob + RS::O_P + pt_frag(2, 1, l));
+        ptf[5] = ld<bf16x8>(ob + RS::O_P + pt_frag(3, 1, l));
+      }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < NB; ++m)
 #pragma unroll
         for (int i = 0; i <= m; ++i)
           rb[m * (m + 1) / 2 + i] = ld<bf16x4>((m == i ? ob + RS::O_TT + 512 * i : rbuf + 512 * m_block(m, i)) + lb_m);
@@ -414,35 +432,40 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
           bf16x8 dhb[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) dhb[kb] = ld<bf16x8>(tb + LY::T_DS + sfrag + (lb_frag ^ (64 * kb)));
-          f32x4 dvp[4];
+          f32x4 dvp[NB];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < NB; ++t) {
             f32x4 yd = zero4();
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) yd = mma32(yd, kf[t][kb], dhb[kb]);
             dvp[t] = w4(t) * yd;
           }
           // dV' += P^T dO (token blocks kb >= t / 2)
-          bf16x8 dob[2];
+          bf16x8 dob[NKB];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
             dob[kb] = cat(ld_tr(tb + LY::T_DO + 2048 * kb + lb_dtr[0]), ld_tr(tb + LY::T_DO + 2048 * kb + lb_dtr[1]));
-          dvp[0] = mma32(mma32(dvp[0], ptf[0], dob[0]), ptf[1], dob[1]);
-          dvp[1] = mma32(mma32(dvp[1], ptf[2], dob[0]), ptf[3], dob[1]);
-          dvp[2] = mma32(dvp[2], ptf[4], dob[1]);
-          dvp[3] = mma32(dvp[3], ptf[5], dob[1]);
+          if constexpr (NB == 4) {
+            dvp[0] = mma32(mma32(dvp[0], ptf[0], dob[0]), ptf[1], dob[1]);
+            dvp[1] = mma32(mma32(dvp[1], ptf[2], dob[0]), ptf[3], dob[1]);
+            dvp[2] = mma32(dvp[2], ptf[4], dob[1]);
+            dvp[3] = mma32(dvp[3], ptf[5], dob[1]);
+          } else {
+            dvp[0] = mma32(dvp[0], ptf[0], dob[0]);
+            dvp[1] = mma32(dvp[1], ptf[2], dob[0]);
+          }
           // Y = R^T dV', as Y_i^T = sum_{m>=i} dV'_m^T R_mi so that lane (n, g)
           // holds columns 4g .. 4g + 3 of token 16i + n;  dX = diag(beta) Y = dv
-          bf16x4 db16[4];
+          bf16x4 db16[NB];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) db16[m] = cvt4(dvp[m]);
+          for (int m = 0; m < NB; ++m) db16[m] = cvt4(dvp[m]);
           float *dvb = p.dv + (row0 * H + h) * (size_t)DV + TC * s + 16 * cs + 4 * g;  // + token row
           const uint32_t yb = xbuf(s) + 4096;
 #pragma unroll
-          for (int i = 3; i >= 0; --i) {
+          for (int i = NB - 1; i >= 0; --i) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int m = 3; m >= i; --m) acc = mma16(acc, db16[m], rb[m * (m + 1) / 2 + i]);
+            for (int m = NB - 1; m >= i; --m) acc = mma16(acc, db16[m], rb[m * (m + 1) / 2 + i]);
             st<bf16x4>(yb + 1024 * i + lb_xw, cvt4(acc));
             const int r = 16 * i + n;
             if (r < L)
@@ -456,10 +479,10 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     __syncthreads();  // dPG^T, F^T and the reductions are complete
 
     // dk (column part) of token rows 16w .. 16w + 15: dPG^T Q + F^T K
-    {
-      bf16x8 pgt[2], ft[2];
+    if (w < NB) {
+      bf16x8 pgt[NKB], ft[NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         pgt[kb] = ld<bf16x8>(fin + pt_frag(w, kb, l));
         ft[kb] = ld<bf16x8>(fin + 8192 + pt_frag(w, kb, l));
       }
@@ -467,7 +490,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 dk = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
           const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
           const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
           const bf16x8 qt = cat(ld_tr(sb + LY::O_Q + a0), ld_tr(sb + LY::O_Q + a1));
@@ -482,14 +505,15 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       const int r = l;
       float ce = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) ce += ld<float>(red + 256 * ww + 4 * r);
+      for (int ww = 0; ww < NB; ++ww) ce += ld<float>(red + 256 * ww + 4 * r);
       const float xyr = ld<float>(red + 1024 + 4 * r) + ld<float>(red + 1280 + 4 * r);
-      float db = ld<float>(red + 2048 + 4 * r) + ld<float>(red + 2816 + 4 * r) - ce;
-      if (r == CH - 1) {
+      // rows past a 32-token chunk hold no token (and reductions nothing wrote)
+      float db = r < CHN ? ld<float>(red + 2048 + 4 * r) + ld<float>(red + 2816 + 4 * r) - ce : 0.f;
+      if (r == CHN - 1) {
         float s3t = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) s3t += ld<float>(red + 2560 + 4 * ww);
-        const float g63 = GATED ? ld<float>(cgt + CG_GS + 4 * (CH - 1)) : 1.f;
+        for (int ww = 0; ww < NB; ++ww) s3t += ld<float>(red + 2560 + 4 * ww);
+        const float g63 = GATED ? ld<float>(cgt + CG_GS + 4 * (CHN - 1)) : 1.f;
         db += s3t + g63 * ld<float>(red + 2576);
       }
       const float incl = wave_incl_scan(db);
@@ -523,19 +547,21 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
   } else {
     // ============================= row waves =============================
     const int rho = w == 4 ? 3 : w == 5 ? 0 : w == 6 ? 2 : 1;  // token rows 16rho .. 16rho + 15
+    // with 32-token chunks the waves of rows 32 .. 63 only issue tile loads
+    const bool active = NB == 4 || rho < NB;
     const bool hdh_wave = rho == 0;
     const uint32_t lb_dfrag = (16 * rho + n) * 64 + 16 * (g ^ swz_d32(n));  // dO frag, row 16rho + n
     // dP, dA: lane (n, g) holds rows 16rho + 4g + e, column 16jt + n;
     // dq1 = dO h^T, dk1 = Y h^T, dk2 = V' dh^T: row 16rho + n, columns 16mt + 4g + e
-    f32x4 dP[4], dAc[4], dq1[MT], dk1[MT], dk2[MT];
+    f32x4 dP[NB], dAc[NB], dq1[MT], dk1[MT], dk2[MT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dP[t] = dAc[t] = zero4();
+    for (int t = 0; t < NB; ++t) dP[t] = dAc[t] = zero4();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) dq1[mt] = dk1[mt] = dk2[mt] = zero4();
     float hdh = 0.f;  // <dh, h> partial (one wave)
     for (int s = 0; s <= ntiles; ++s) {
       if (s + 2 < ntiles) issue_tile(s + 2);
-      if (s > 0) {
+      if (s > 0 && active) {
         const int j = s - 1;
         const uint32_t tb = tbuf(j), xv = xbuf(j), xyb = xbuf(j) + 4096;
         const bf16x8 dof = ld<bf16x8>(tb + LY::T_DO + lb_dfrag);
@@ -543,7 +569,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         // every token block: the blocks above the diagonal (jt > rho) are masked in the final phase
         bf16x8 vf;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < NB; ++jt) {
           const bf16x8 vt = ld<bf16x8>(xv + 1024 * jt + lb_xf);
           if (jt == rho) vf = vt;
           dP[jt] = mma32(dP[jt], dof, vt);
@@ -561,20 +587,23 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         }
       }
       // tile s + 1 (and everything older) lands before the barrier; tile s + 2 may stay in flight
-      if (s + 2 < ntiles && full) wait_vm<LY::DMA_T>();
+      if (s + 2 < ntiles && full) wait_tiles(I1{});
       else wait_vm<0>();
       mfma_settle();
       __syncthreads();
     }
 
-    // ---- final phase (row wave rho: rows r = 16rho + 4g + e)
+    // ---- final phase (row wave rho: rows r = 16rho + 4g + e).  With 32-token
+    // chunks the waves of rows 32 .. 63 run the next part too: their results
+    // land in LDS that nothing reads (columns 32 .. 63 of dPG^T and F^T,
+    // reductions of rows past the chunk, which wave 0 leaves out).
     const f32x4 bet_r = bet4(rho);
     float *const dqb = p.dq + ((row0 + 16 * rho) * H + h) * (size_t)DK;  // rows of this block (wave-uniform)
     float *const dkb = p.dk + ((row0 + 16 * rho) * H + h) * (size_t)DK;
     const f32x4 bl_r = GATED ? ld<f32x4>(cgt + CG_BL + 4 * (16 * rho + 4 * g)) : zero4();
     f32x4 erow = zero4(), dbr = zero4();
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
+    for (int jt = 0; jt < NB; ++jt) {
       f32x4 dpg = zero4(), f = zero4();
       float ce = 0.f;
       if (jt <= rho) {
@@ -688,10 +717,10 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
     // as dq^T = gamma dq1^T + K^T dPG^T (and likewise dk): lane (n, g) holds row r = 16rho + n,
     // columns 16mt + 4g .. + 3, written as one 16-byte store
     f32x4 dkr[MT], dqv[MT];  // dqv: PRO only
-    {
-      bf16x8 pgr[2], fr[2];  // B operands: rows r of dPG and F, read transposed from dPG^T, F^T
+    if (active) {
+      bf16x8 pgr[NKB], fr[NKB];  // B operands: rows r of dPG and F, read transposed from dPG^T, F^T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         const int r0 = 32 * kb + 8 * g + e4, r1 = r0 + 4;  // dPG^T rows j
         const int cc = 16 * rho + 4 * q4;                   // columns r
         const uint32_t a0 = 128 * r0 + 16 * ((cc / 8) ^ swz_p128(r0 & 15)) + 8 * ((cc % 8) / 4);
@@ -704,7 +733,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         f32x4 dq = gam_n * dq1[mt];
         f32x4 dk = w_n * dk2[mt] - (gam_n * bet_n) * dk1[mt];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
           const uint32_t a0 = 32 * kb * RB + (lb_str[0] ^ (32 * mt)), a1 = 32 * kb * RB + (lb_str[1] ^ (32 * mt));
           const bf16x8 kt = cat(ld_tr(sb + LY::O_K + a0), ld_tr(sb + LY::O_K + a1));
           dq = mma32(dq, kt, pgr[kb]);
@@ -716,6 +745,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
       }
     }
     if constexpr (PRO) {
+      if (active) {
       mfma_settle();
       pro_norm(dqv, xq);
       if (rr < L) {
@@ -723,9 +753,11 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
         for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dqb + (uint32_t)(n * H * DK + 16 * mt + 4 * g)) = dqv[mt];
       }
     }
+    }
     mfma_settle();
     __syncthreads();  // the column part of dk is in LDS
-    if constexpr (LH) {
+    if (!active) {
+    } else if constexpr (LH) {
       // dk += -2 eps^2 deps k (row rr; k from the chunk's K tile, columns 16mt + 4g ..)
       const float ep = ld<float>(sb + LY::O_BETA + 4 * rr);
       const float c = -2.f * ep * ep * (rr < L ? ld<float>(red + 3072 + 4 * rr) : 0.f);
@@ -759,9 +791,12 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_chunk_kernel(BwdParams p) {
 template <int DK>
 hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   const size_t smem = BLay<DK>::TOTAL;
-  auto kern = p.q_in       ? (p.g ? bwd_chunk_kernel<DK, true, EPI_PRO> : bwd_chunk_kernel<DK, false, EPI_PRO>)
-              : p.beta_raw ? (p.g ? bwd_chunk_kernel<DK, true, EPI_LH> : bwd_chunk_kernel<DK, false, EPI_LH>)
-                           : (p.g ? bwd_chunk_kernel<DK, true, EPI_PLAIN> : bwd_chunk_kernel<DK, false, EPI_PLAIN>);
+  // 32-token chunks: the plain gradients only
+  if (p.chunk == 32 && (p.q_in || p.beta_raw)) return hipErrorInvalidValue;
+  auto kern = p.chunk == 32  ? (p.g ? bwd_chunk_kernel<DK, true, EPI_PLAIN, 2> : bwd_chunk_kernel<DK, false, EPI_PLAIN, 2>)
+              : p.q_in       ? (p.g ? bwd_chunk_kernel<DK, true, EPI_PRO, 4> : bwd_chunk_kernel<DK, false, EPI_PRO, 4>)
+              : p.beta_raw ? (p.g ? bwd_chunk_kernel<DK, true, EPI_LH, 4> : bwd_chunk_kernel<DK, false, EPI_LH, 4>)
+                           : (p.g ? bwd_chunk_kernel<DK, true, EPI_PLAIN, 4> : bwd_chunk_kernel<DK, false, EPI_PLAIN, 4>);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;

@@ -223,9 +223,9 @@ __device__ __forceinline__ void prep32(const Bases &lb, uint32_t kbase, uint32_t
 
 // ---------------------------------------------------------------- chain
 
-template <int DK, bool GATED>
+template <int DK, bool GATED, bool STORE_STATES, bool WRITE_O>
 __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32x4 (&hs)[DK / 16], uint32_t slot,
-                                        uint32_t ob, int L, size_t row0, int h, int col) {
+                                        uint32_t ob, int L, size_t row0, int h, int col, bf16 *states_dst) {
   using LY = Lay32<DK>;
   constexpr int KB = LY::KB, MT = LY::MT;
   const int l = lane_id(), n = l & 15, g = l >> 4;
@@ -245,7 +245,7 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         kf[t][kb] = ld<bf16x8>(a + LY::S_K + 16 * t * LY::RB);
-        qf[t][kb] = ld<bf16x8>(a + LY::S_Q + 16 * t * LY::RB);
+        if constexpr (WRITE_O) qf[t][kb] = ld<bf16x8>(a + LY::S_Q + 16 * t * LY::RB);
       }
     }
 #pragma unroll
@@ -255,7 +255,7 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         yk[t] = mma32(yk[t], kf[t][kb], hb[kb]);
-        yq[t] = mma32(yq[t], hb[kb], qf[t][kb]);
+        if constexpr (WRITE_O) yq[t] = mma32(yq[t], hb[kb], qf[t][kb]);
       }
     }
   }
@@ -279,7 +279,7 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
     vb[1] = cvt4(vp[1]);
   }
   // O^T = diag(gamma s_c) Y_Q^T + V'^T P^T: lane (n, g) holds O[16nt + n][16w + 4g + e]
-  {
+  if constexpr (WRITE_O) {
     bf16 *orow = static_cast<bf16 *>(p.o) + (row0 * H + h) * (size_t)DV + (col - n) + 4 * g;
     const bf16x8 va = cat(vb[0], vb[1]);
 #pragma unroll
@@ -289,6 +289,15 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
       acc = mma32(acc, va, ld<bf16x8>(ob + LY::O_P + p_read(lb, nt, 0)));
       if (16 * nt + n < L) *reinterpret_cast<bf16x4 *>(orow + (size_t)(16 * nt + n) * H * DV) = cvt4(acc);
     }
+  }
+  // the state at the chunk start, h = s_c h~, as S = h^T in bf16 (the layout
+  // of the 64-token kernel's stored states, one state per 32-token chunk)
+  if constexpr (STORE_STATES) {
+    const float sc = GATED ? ld<float>(ob + LY::O_CG + CG_SC) : 1.f;
+    bf16 *dst = states_dst + (size_t)col * DK + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      *reinterpret_cast<bf16x8 *>(dst + 32 * kb) = bfrag<bf16>(hs[2 * kb] * sc, hs[2 * kb + 1] * sc);
   }
   // h~ <- h~ + K^T diag(w / s_{c+1}) V'   (after h~ *= gamma_31 s_c on a rescale)
   bf16x8 wb;
@@ -320,7 +329,7 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
 
 // ---------------------------------------------------------------- kernel
 
-template <int DK, bool GATED>
+template <int DK, bool GATED, bool STORE_STATES, bool WRITE_O>
 __global__ __launch_bounds__(F32_THREADS, 1) void fwd32_kernel(FwdParams p) {
   using LY = Lay32<DK>;
   constexpr int MT = LY::MT;
@@ -412,6 +421,8 @@ __global__ __launch_bounds__(F32_THREADS, 1) void fwd32_kernel(FwdParams p) {
       hs[mt][i] = (chain && p.h0) ? p.h0[st_base + (size_t)r * DV + col] : 0.f;
     }
   float scale = 1.f;  // prep wave 0: state scale s_c of the next chunk it prepares
+  // global chunk index of the sequence's first chunk (state slots)
+  const int cg0 = STORE_STATES ? (p.chunk_base ? p.chunk_base[n_seq] : n_seq * p.NC) : 0;
 
   if (!chain) {
     for (int cc = 0; cc < AHEAD - 1 && cc < nch; ++cc) issue(cc);
@@ -427,7 +438,10 @@ __global__ __launch_bounds__(F32_THREADS, 1) void fwd32_kernel(FwdParams p) {
         const uint32_t slot = sbase + (uint32_t)(s % NBUF32) * LY::SLOT;
         const uint32_t ob = sbase + LY::OUT_OFF + (uint32_t)(s & 1) * LY::OUTB;
         const int L = min(C32, si.len - s * C32);
-        chain32<DK, GATED>(p, lb, hs, slot, ob, L, row_base + (size_t)s * C32, h, col);
+        bf16 *sdst = nullptr;
+        if (STORE_STATES) sdst = p.states + ((size_t)(cg0 + s) * H + h) * (size_t)DV * DK;
+        chain32<DK, GATED, STORE_STATES, WRITE_O>(p, lb, hs, slot, ob, L, row_base + (size_t)s * C32, h, col,
+                                                  sdst);
       }
     } else {
       if (s + AHEAD < nch) issue(s + AHEAD);
@@ -467,10 +481,10 @@ __global__ __launch_bounds__(F32_THREADS, 1) void fwd32_kernel(FwdParams p) {
   }
 }
 
-template <int DK>
+template <int DK, bool STORE_STATES, bool WRITE_O>
 hipError_t launch32_t(const FwdParams &p, hipStream_t stream) {
   const size_t smem = Lay32<DK>::TOTAL;
-  auto kern = p.g ? fwd32_kernel<DK, true> : fwd32_kernel<DK, false>;
+  auto kern = p.g ? fwd32_kernel<DK, true, STORE_STATES, WRITE_O> : fwd32_kernel<DK, false, STORE_STATES, WRITE_O>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -482,10 +496,16 @@ hipError_t launch32_t(const FwdParams &p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fwd_c32(const FwdParams &p, int DK, hipStream_t stream) {
-  if (DK == 64) return launch32_t<64>(p, stream);
-  if (DK == 128) return launch32_t<128>(p, stream);
+hipError_t launch_fwd_c32(const FwdParams &p, int DK, bool store_states, bool write_o, hipStream_t stream) {
+#define DN_FWD32_CASE(D)                                                 \
+  if (store_states)                                                      \
+    return write_o ? launch32_t<D, true, true>(p, stream)                \
+                   : launch32_t<D, true, false>(p, stream);              \
+  return write_o ? launch32_t<D, false, true>(p, stream) : hipErrorInvalidValue;
+  if (DK == 64) { DN_FWD32_CASE(64) }
+  if (DK == 128) { DN_FWD32_CASE(128) }
   return hipErrorInvalidValue;
+#undef DN_FWD32_CASE
 }
 
 }  // namespace dn

@@ -34,6 +34,7 @@ struct BwdParams {
   int B, T, H, DV, N, NC;
   int ntiles, xcd_map;
   int total_chunks;           // upper bound of chunks (grid of the chunk-parallel pass)
+  int chunk;                  // chunk length: 64, or 32 for the plain gradients
   // input prologue folded into the chunk-gradient kernel (q_in set): dq, dk,
   // dbeta, dg receive the gradients of q_in, k_in, b_in, x_in instead
   const void *q_in, *k_in;
@@ -128,7 +129,7 @@ size_t fwd_ref_smem_bytes(int dtype, int DK);
 hipError_t launch_fwd(const FwdParams &p, int dtype, int DK, bool store_states, bool write_o,
                       hipStream_t stream);
 // the forward pass with 32-token chunks (bf16)
-hipError_t launch_fwd_c32(const FwdParams &p, int DK, hipStream_t stream);
+hipError_t launch_fwd_c32(const FwdParams &p, int DK, bool store_states, bool write_o, hipStream_t stream);
 hipError_t launch_fwd_ref(const FwdParams &p, int dtype, int DK, bool store_states,
                           bool write_o, hipStream_t stream);
 hipError_t launch_step(const StepParams &p, int dtype, int DK, hipStream_t stream);
@@ -137,7 +138,7 @@ hipError_t launch_prologue(const PrologueParams &p, int dtype, int DK, bool back
 // forward (y) or backward (dx, dw; dw is cleared first); W in 1..4
 hipError_t launch_conv(const ConvParams &p, int dtype, bool backward, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
-                              int max_chunks, hipStream_t stream);
+                              int max_chunks, int chunk, hipStream_t stream);
 // ev_scan / ev_chunk (may be null) are recorded on `stream` after the scan and
 // after the chunk-gradient kernel
 hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream, hipEvent_t ev_scan = nullptr,

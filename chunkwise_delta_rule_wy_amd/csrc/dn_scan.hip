@@ -61,12 +61,13 @@ struct ScanKsw {
 
 // ---------------------------------------------------------------- chain
 
-template <int DK, bool GATED>
+template <int DK, bool GATED, int NB>
 __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16], uint32_t slot, uint32_t ob,
                                             const uint32_t (&dtr)[2], const uint32_t (&dpr)[2], bf16 *dst) {
   using LY = SLay<DK>;
   using RS = Res<MODE_SCAN>;
   constexpr int KB = LY::KB, MT = LY::MT;
+  constexpr int NKB = NB / 2;  // 32-token contraction blocks of the chunk
   const int l = lane_id(), g = l >> 4;
   const uint32_t cgt = ob + RS::O_CG;
 
@@ -82,40 +83,40 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
   for (int kb = 0; kb < KB; ++kb) hb[kb] = bfrag<bf16>(hs[2 * kb], hs[2 * kb + 1]);
 
   // dV' = diag(w s) K dh~ + P^T dO (lane (n, g): row 16t + 4g + e, column 16w + n)
-  f32x4 dvp[4];
+  f32x4 dvp[NB];
   {
-    bf16x8 kf[4][KB];
+    bf16x8 kf[NB][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint32_t a = (lb.frag ^ (64 * kb)) + slot + LY::S_K;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kf[t][kb] = ld<bf16x8>(a + 16 * t * LY::RB);
+      for (int t = 0; t < NB; ++t) kf[t][kb] = ld<bf16x8>(a + 16 * t * LY::RB);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NB; ++t) {
       f32x4 yd = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) yd = mma32(yd, kf[t][kb], hb[kb]);
       dvp[t] = GATED ? yd * ld<f32x4>(cgt + CG_WS + 4 * (16 * t + 4 * g)) : yd;
     }
   }
-  bf16x8 dob[2];
+  bf16x8 dob[NKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
     dob[kb] = cat(ld_tr(slot + LY::S_D + 32 * kb * 128 + dtr[0]), ld_tr(slot + LY::S_D + 32 * kb * 128 + dtr[1]));
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < NB; ++t)
 #pragma unroll
-    for (int kb = t >> 1; kb < 2; ++kb) dvp[t] = mma32(dvp[t], ld<bf16x8>(ob + RS::O_P + pt_frag(t, kb, l)), dob[kb]);
+    for (int kb = t >> 1; kb < NKB; ++kb) dvp[t] = mma32(dvp[t], ld<bf16x8>(ob + RS::O_P + pt_frag(t, kb, l)), dob[kb]);
 
   // dX_i = diag(beta_i) R_ii^T (dV'_i - sum_{m>i} M_mi^T dX_m)
-  f32x4 dx[4];
-  bf16x4 dxb[4];
+  f32x4 dx[NB];
+  bf16x4 dxb[NB];
 #pragma unroll
-  for (int i = 3; i >= 0; --i) {
+  for (int i = NB - 1; i >= 0; --i) {
     f32x4 acc = dvp[i];
 #pragma unroll
-    for (int m = i + 1; m < 4; ++m) acc = mma16(acc, ld_tr(ob + RS::O_M + 512 * m_block(m, i) + lb.btr), dxb[m]);
+    for (int m = i + 1; m < NB; ++m) acc = mma16(acc, ld_tr(ob + RS::O_M + 512 * m_block(m, i) + lb.btr), dxb[m]);
     const f32x4 y = mma16(zero4(), ld<bf16x4>(ob + RS::O_TT + 512 * i + lb.m), cvt4(acc));
     dx[i] = y * ld<f32x4>(slot + LY::S_BETA + 4 * (16 * i + 4 * g));
     dxb[i] = cvt4(dx[i]);
@@ -123,9 +124,9 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
 
   // dh~ <- dh~ + Q^T diag(gamma / s) dO - K^T diag(gamma / s) dX (after dh~ *= gamma_63 s on a restart);
   // contraction slot 8g + s of block kb is token 32kb + 16(s/4) + 4g + s%4
-  bf16x8 bo[2], bx[2];
+  bf16x8 bo[NKB], bx[NKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     bf16x4 part[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -161,7 +162,7 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
     f32x4 acc = hs[mt];
     const uint32_t aoff = 8 * (mt & 1) + (lb.ktr ^ (64 * (mt >> 1)));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       const uint32_t r0 = 32 * kb * LY::RB, r1 = (32 * kb + 16) * LY::RB;
       const bf16x8 qt = cat(ld_tr(slot + LY::S_Q + aoff + r0), ld_tr(slot + LY::S_Q + aoff + r1));
       const bf16x8 kt = cat(ld_tr(slot + LY::S_K + aoff + r0), ld_tr(slot + LY::S_K + aoff + r1));
@@ -175,10 +176,13 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
 
 // ---------------------------------------------------------------- kernel
 
-template <int DK, bool GATED>
+template <int DK, bool GATED, int NB>
 __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p) {
   using LY = SLay<DK>;
   constexpr int MT = LY::MT;
+  constexpr int CHN = 16 * NB;               // tokens per chunk (64 or 32)
+  constexpr int NKQ = LY::DMA_KQ * NB / 4;   // direct loads per prep wave of a chunk's K (or Q) rows
+  constexpr int ND = LY::DMA_D * NB / 4;     // ... and of its dO rows
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const uint32_t sbase = (uint32_t)(uintptr_t)(lds_ptr<unsigned char>)smem_raw;
 
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
   const int n_seq = pair / p.H, h = pair % p.H;
   const int dv0 = tile * DVT;
   const SeqInfo si = seq_info(p.cu, n_seq, p.T);
-  const int nch = (si.len + CH - 1) / CH;
+  const int nch = (si.len + CHN - 1) / CHN;
   const int H = p.H, DV = p.DV;
 
   const int w = wave_id(), l = lane_id(), n = l & 15, g = l >> 4, e4 = (l >> 2) & 3, q4 = l & 3;
@@ -238,29 +242,32 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
   auto issue = [&](int o, int part) {
     const int cc = chunk_of(o);
     const uint32_t slot = slot_of(o);
-    const int Lc = min(CH, si.len - cc * CH);
-    const size_t r0 = row_base + (size_t)cc * CH;
+    const int Lc = min(CHN, si.len - cc * CHN);
+    const size_t r0 = row_base + (size_t)cc * CHN;
     const char *kb_ = gk + (r0 * H + h) * (size_t)(DK * 2);
     const char *qb_ = gq + (r0 * H + h) * (size_t)(DK * 2);
     const char *db_ = gdo + ((r0 * H + h) * (size_t)DV + dv0) * 2;
     const float *sp = v == 0 ? p.g : p.beta;
     const bool scal = (v == 1) || (GATED && v == 0);
     const uint32_t sdst = slot + (v == 0 ? LY::S_G : LY::S_BETA);
-    if (Lc == CH) {
-      constexpr int KH = (LY::DMA_KQ + 1) / 2;
+    if (Lc == CHN) {
+      // load i of a prep wave covers rows below CHN exactly when i < NKQ (ND)
+      constexpr int KH = (NKQ + 1) / 2;
       if (part == 0) {
 #pragma unroll
         for (int i = 0; i < KH; ++i) dma16s(kb_, koff[i], slot + LY::S_K + 1024 * (v + 4 * i));
-        if (scal) dma4(reinterpret_cast<const char *>(sp + r0 * H + h) + soff, sdst);
+        // one lane per row of the chunk: with 32-token chunks lanes 32 .. 63
+        // would read the rows after it, past the end of the last chunk
+        if (scal && (NB == 4 || l < CHN)) dma4(reinterpret_cast<const char *>(sp + r0 * H + h) + soff, sdst);
       } else if (part == 1) {
 #pragma unroll
-        for (int i = KH; i < LY::DMA_KQ; ++i) dma16s(kb_, koff[i], slot + LY::S_K + 1024 * (v + 4 * i));
+        for (int i = KH; i < NKQ; ++i) dma16s(kb_, koff[i], slot + LY::S_K + 1024 * (v + 4 * i));
       } else if (part == 2) {
 #pragma unroll
-        for (int i = 0; i < LY::DMA_KQ; ++i) dma16s(qb_, koff[i], slot + LY::S_Q + 1024 * (v + 4 * i));
+        for (int i = 0; i < NKQ; ++i) dma16s(qb_, koff[i], slot + LY::S_Q + 1024 * (v + 4 * i));
       } else {
 #pragma unroll
-        for (int i = 0; i < LY::DMA_D; ++i) dma16s(db_, doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
+        for (int i = 0; i < ND; ++i) dma16s(db_, doff[i], slot + LY::S_D + 1024 * (v + 4 * i));
       }
     } else if (part == 0) {
 #pragma unroll
@@ -282,13 +289,13 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
         st<f32x4>(slot + LY::S_Q + 16 * i, zero4());
       }
       for (int i = Lc * 128 / 16 + tp; i < LY::DT / 16; i += 4 * 64) st<f32x4>(slot + LY::S_D + 16 * i, zero4());
-      if (tp < CH && tp >= Lc) {
+      if (tp < CHN && tp >= Lc) {
         st<float>(slot + LY::S_G + 4 * tp, 0.f);
         st<float>(slot + LY::S_BETA + 4 * tp, 0.f);
       }
     }
   };
-  auto full = [&](int o) { return (chunk_of(o) + 1) * CH <= si.len; };
+  auto full = [&](int o) { return (chunk_of(o) + 1) * CHN <= si.len; };
 
   // chain waves: dh~ slice, lane (n, g) holds rows prow(mt, 4g + i) of column `col`
   f32x4 hs[MT];
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
         const int c = chunk_of(s);
         const uint32_t ob = sbase + LY::OUT_OFF + (uint32_t)(s & 1) * LY::OUTB;
         bf16 *dst = p.dstates + (((size_t)(cg0 + c) * H + h) * DV + col) * DK + 8 * g;
-        chain_chunk<DK, GATED>(lb, hs, slot_of(s), ob, dtr, dpr, dst);
+        chain_chunk<DK, GATED, NB>(lb, hs, slot_of(s), ob, dtr, dpr, dst);
       }
     } else {
       const bool iss_now = s + 2 < nch;
@@ -331,17 +338,17 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
         const uint32_t slot = slot_of(o);
         const uint32_t ob = sbase + LY::OUT_OFF + (uint32_t)(o & 1) * LY::OUTB;
         const uint32_t priv = sbase + LY::PRIV_OFF + (uint32_t)v * PRIV_BYTES;
-        const int L = min(CH, si.len - c * CH);
+        const int L = min(CHN, si.len - c * CHN);
         const ScanKsw<DK> ksw{lb.frag};
         const uint32_t ka = slot + LY::S_K, qa = slot + LY::S_Q, ga = slot + LY::S_G, ba = slot + LY::S_BETA;
-        if (v == 0) prep_chunk<DK, GATED, true, MODE_SCAN, 0>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
-        else if (v == 1) prep_chunk<DK, GATED, true, MODE_SCAN, 1>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
-        else if (v == 2) prep_chunk<DK, GATED, true, MODE_SCAN, 2>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
-        else prep_chunk<DK, GATED, true, MODE_SCAN, 3>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        if (v == 0) prep_chunk<DK, GATED, true, MODE_SCAN, 0, NB>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        else if (v == 1) prep_chunk<DK, GATED, true, MODE_SCAN, 1, NB>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        else if (v == 2) prep_chunk<DK, GATED, true, MODE_SCAN, 2, NB>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
+        else prep_chunk<DK, GATED, true, MODE_SCAN, 3, NB>(lb, ka, qa, ga, ba, ob, priv, L, scale, ksw, iss);
       }
       // K, Q, g, beta of order s + 2 (and everything older) land before the
       // barrier; its dO may stay in flight until the next one
-      if (s + 2 < nch && full(s + 2)) wait_vm<LY::DMA_D>();
+      if (s + 2 < nch && full(s + 2)) wait_vm<ND>();
       else wait_vm<0>();
     }
     __syncthreads();
@@ -361,10 +368,10 @@ __global__ __launch_bounds__(SCAN_THREADS, 1) void scan_bf16_kernel(BwdParams p)
   }
 }
 
-template <int DK>
+template <int DK, int NB>
 hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
   const size_t smem = SLay<DK>::TOTAL;
-  auto kern = p.g ? scan_bf16_kernel<DK, true> : scan_bf16_kernel<DK, false>;
+  auto kern = p.g ? scan_bf16_kernel<DK, true, NB> : scan_bf16_kernel<DK, false, NB>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
@@ -377,8 +384,13 @@ hipError_t launch_t(const BwdParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_scan(const BwdParams &p, int DK, hipStream_t stream) {
-  if (DK == 64) return launch_t<64>(p, stream);
-  if (DK == 128) return launch_t<128>(p, stream);
+  if (p.chunk == 32) {
+    if (DK == 64) return launch_t<64, 2>(p, stream);
+    if (DK == 128) return launch_t<128, 2>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  if (DK == 64) return launch_t<64, 4>(p, stream);
+  if (DK == 128) return launch_t<128, 4>(p, stream);
   return hipErrorInvalidValue;
 }
 

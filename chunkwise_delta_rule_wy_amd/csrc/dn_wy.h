@@ -219,13 +219,18 @@ using I1 = std::integral_constant<int, 1>;
 using I2 = std::integral_constant<int, 2>;
 using I3 = std::integral_constant<int, 3>;
 
-// Preparation of one chunk by one of four waves (PW).
+// Preparation of one chunk of NB 16-token blocks (NB = 4: 64 tokens; NB = 2:
+// 32 tokens) by one of four waves (PW).
 //
-//   every wave:  diagonal block M_vv (fp32, into its A^T scratch) and the
+//   wave v < NB: diagonal block M_vv (fp32, into its A^T scratch) and the
 //                inverse of its diagonal block by forward substitution;
 //                P_vv
 //   wave 0: -M_10 -M_20 -M_30    wave 1: -M_21 -M_31 -M_32
 //   wave 2: P_10 P_20 P_21       wave 3: P_30 P_31 P_32
+//
+// (every block with an index >= NB is left out).  For NB = 2 the rows
+// 32 .. 63 are outside the chunk: the gate scan adds zero over them, so the
+// value of lane 63 is the chunk's last cumulative gate b_31.
 //
 // M = strictLower((K K^T) * Gamma), P = (Q K^T) * Gamma (lower, with the
 // diagonal), A = diag(beta) M.  The forward variant stores T_vv =
@@ -235,10 +240,11 @@ using I3 = std::integral_constant<int, 3>;
 // M_vv^T and the plain gate table, the scan one the gate table of the scaled
 // state gradient.  kbase, qbase: K and Q tiles (K-tile swizzle KSW); gaddr, baddr:
 // g and beta of the chunk's rows (fp32, LDS); rows >= L are padding.
-template <int DK, bool GATED, bool WRITE_P, int MODE, int PW, typename KSW, typename ISS = NoIssue>
+template <int DK, bool GATED, bool WRITE_P, int MODE, int PW, int NB = 4, typename KSW, typename ISS = NoIssue>
 __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint32_t qbase, uint32_t gaddr,
                                            uint32_t baddr, uint32_t ob, uint32_t priv, int L, float &scale,
                                            KSW ksw, ISS iss = ISS{}) {
+  static_assert(NB == 4 || NB == 2, "64- or 32-token chunks");
   using RS = Res<MODE>;
   constexpr bool BWD = MODE != MODE_FWD;
   constexpr int KB = DK / 32;
@@ -287,16 +293,16 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
   }
   iss(0);
 
-  bf16x8 kf[4][KB];  // K rows 16t + n, d_k block kb
+  bf16x8 kf[NB][KB];  // K rows 16t + n, d_k block kb
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kf[t][kb] = ld<bf16x8>(kbase + ksw.frag(t, kb));
+    for (int t = 0; t < NB; ++t) kf[t][kb] = ld<bf16x8>(kbase + ksw.frag(t, kb));
 
   // Diagonal block PW of A = strictLower(diag(beta) (K K^T) * Gamma), fp32,
   // transposed into the scratch.  Lane (n, g) holds k_r . k_j with
   // r = 16PW + 4g + e, j = 16PW + n.
-  {
+  if constexpr (PW < NB) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) acc = mma32(acc, kf[PW][kb], kf[PW][kb]);
@@ -326,6 +332,7 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
   // r = 16TI + n, j = 16TJ + 4g + e.
   auto mtile = [&](auto ti_c, auto tj_c) {
     constexpr int TI = decltype(ti_c)::value, TJ = decltype(tj_c)::value;
+    if constexpr (TI < NB) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) acc = mma32(acc, kf[TJ][kb], kf[TI][kb]);
@@ -338,6 +345,7 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
       v = -acc;
     }
     st<bf16x4>(ob + RS::O_M + 512 * m_block(TI, TJ) + lb.m, cvt4(v));
+    }
   };
   // in the scan, wave 0 (which also keeps the scale bookkeeping) hands block
   // (3, 0) to wave 2, the prep wave with the least other work there
@@ -361,6 +369,7 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
     // holds q_r . k_j with r = 16TI + 4g + e, j = 16TJ + n, stored into P^T.
     auto ptile = [&](auto ti_c, auto tj_c, const bf16x8(&qf)[KB]) {
       constexpr int TI = decltype(ti_c)::value, TJ = decltype(tj_c)::value;
+      if constexpr (TI < NB) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc = BWD ? mma32(acc, qf[kb], kf[TJ][kb]) : mma32(acc, kf[TJ][kb], qf[kb]);
@@ -390,10 +399,13 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
       }
       if constexpr (BWD) st<bf16x4>(ob + RS::O_P + pt_quad(TJ, TI, l), cvt4(v));
       else st<bf16x4>(ob + RS::O_P + p_write<TI, TJ>(lb), cvt4(v));
+      }
     };
     auto qfrag = [&](bf16x8(&qf)[KB], int ti) {
+      if (ti < NB) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) qf[kb] = ld<bf16x8>(qbase + ksw.frag(ti, kb));
+        for (int kb = 0; kb < KB; ++kb) qf[kb] = ld<bf16x8>(qbase + ksw.frag(ti, kb));
+      }
     };
     bf16x8 qa[KB], qb[KB];
     if constexpr (PW == 0) {
@@ -424,7 +436,7 @@ __device__ __forceinline__ void prep_chunk(const Bases &lb, uint32_t kbase, uint
   // (l / 4, l % 4) holds rows 4qr .. 4qr + 3 of column c; column j of A_vv is
   // read from the scratch and x_j is broadcast from its owner lane of the quad.
   wave_lds_fence();
-  {
+  if constexpr (PW < NB) {
     const int c = l >> 2, qr = l & 3;
     float x[4];
 #pragma unroll

@@ -156,6 +156,29 @@ int main() {
                                F(32), F(33), F(34), F(35), P(40), ws, nullptr, nullptr),
          DN_EINVAL, 0);
 
+  // ---- 32-token chunks: the training pair and the backward pass (ceil(300 / 32) = 10 chunks per sequence)
+  s = shape(2, 300, 4, 128, 256, 2, 32, DN_BF16);
+  const size_t ws32 = dn_chunk_bwd_workspace(&s);
+  if (ws32 != 2 * (size_t)(2 * 10) * 4 * 128 * 256 * 2) {
+    fprintf(stderr, "32-token workspace %zu\n", ws32);
+    return 1;
+  }
+  EXPECT(bwd(&s, nullptr, ws32), DN_OK, 2);
+  EXPECT(bwd(&s, nullptr, ws), DN_ENOWS, 0);  // sized for 64-token chunks
+  EXPECT(dn_chunk_fwd_save(&s, P(1), P(2), P(3), F(4), F(5), F(6), nullptr, P(20), F(21), P(40), ws32, nullptr),
+         DN_OK, 1);
+  EXPECT(dn_chunk_bwd_saved(&s, P(1), P(2), P(3), F(4), F(5), F(6), nullptr, P(7), F(8), F(30), F(31), F(32),
+                            F(33), F(34), F(35), P(40), ws32, nullptr, nullptr),
+         DN_OK, 1);
+  EXPECT(dn_chunk_bwd_prologue(&s, P(1), P(2), P(3), F(4), F(5), F(6), nullptr, P(7), F(8), P(11), P(12), F(13),
+                               0.1f, F(30), F(31), F(32), F(33), F(34), F(35), P(40), ws32, nullptr, nullptr),
+         DN_EUNSUPPORTED, 0);  // the folded variants take 64-token chunks
+  EXPECT(dn_chunk_bwd_longhorn(&s, P(1), P(2), P(3), F(4), F(5), F(6), nullptr, P(7), F(8), F(14), F(30), F(31),
+                               F(32), F(33), F(34), F(35), P(40), ws32, nullptr, nullptr),
+         DN_EUNSUPPORTED, 0);
+  s = shape(1, 300, 4, 128, 256, 5, 32, DN_BF16);
+  EXPECT(bwd(&s, cu, dn_chunk_bwd_workspace(&s)), DN_OK, 3);  // chunk table, recompute, backward
+
   // ---- decode step
   EXPECT(dn_recurrent_step(256, 32, 128, 128, DN_BF16, P(1), P(2), P(3), F(4), F(5), F(6), P(7), nullptr), DN_OK,
          1);

@@ -11,13 +11,13 @@ namespace dn {
 size_t fwd_smem_bytes(int, int) { return 0; }
 size_t fwd_ref_smem_bytes(int, int) { return 0; }
 hipError_t launch_fwd(const FwdParams &, int, int, bool, bool, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_fwd_c32(const FwdParams &, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_fwd_c32(const FwdParams &, int, bool, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fwd_ref(const FwdParams &, int, int, bool, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_step(const StepParams &, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_longhorn(const LonghornParams &, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prologue(const PrologueParams &, int, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_conv(const ConvParams &, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_chunk_table(const int32_t *, int, int32_t *, int32_t *, int, hipStream_t) {
+hipError_t launch_chunk_table(const int32_t *, int, int32_t *, int32_t *, int, int, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }

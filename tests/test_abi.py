@@ -81,10 +81,18 @@ def test_fwd_accepts_largest_chunk_span(lib):
     assert fwd(lib, shape(H=8191, Dv=1024), o=None) == DN_EINVAL
 
 
-def test_fwd_takes_32_token_chunks_in_bf16(lib):
+def test_32_token_chunks_in_bf16(lib):
     # accepted by validation (which then fails on the null output)
     assert fwd(lib, shape(chunk=32), o=None) == DN_EINVAL
-    assert fwd_save(lib, shape(chunk=32)) == DN_EUNSUPPORTED  # the training pair is 64-token
+    # the training pair takes them too, with a workspace for twice the chunk states
+    s32, s64 = shape(chunk=32), shape()
+    need32 = lib.dn_chunk_bwd_workspace(ctypes.byref(s32))
+    need64 = lib.dn_chunk_bwd_workspace(ctypes.byref(s64))
+    assert need32 == 2 * need64 > 0
+    assert fwd_save(lib, s32, o=None) == DN_EINVAL
+    assert fwd_save(lib, s32, wsb=need64) == DN_ENOWS
+    assert fwd_save(lib, shape(chunk=32, dtype=0)) == DN_EUNSUPPORTED
+    assert bwd_saved(lib, s32, wsb=need64) == DN_ENOWS
 
 
 def test_fwd_rejects_null_and_misaligned(lib):
@@ -106,7 +114,9 @@ def test_bwd_validation(lib):
     assert bwd(lib, s, wsb=need - 1) == DN_ENOWS
     assert bwd(lib, s, ws=None) == DN_ENOWS
     assert bwd(lib, shape(chunk=128)) == DN_EUNSUPPORTED
-    assert bwd(lib, shape(chunk=32)) == DN_EUNSUPPORTED  # 32-token chunks: forward only
+    assert bwd(lib, shape(chunk=32), q=None) == DN_EINVAL  # accepted chunk length, then the null input
+    assert bwd(lib, shape(chunk=32), wsb=need) == DN_ENOWS  # twice the states of 64-token chunks
+    assert bwd(lib, shape(chunk=32, dtype=0)) == DN_EUNSUPPORTED
 
 
 def test_bwd_workspace_covers_varlen_bound(lib):
@@ -190,7 +200,7 @@ def test_saved_state_pair_validation(lib):
     assert fwd_save(lib, s, o=FAKE + 8) == DN_EINVAL
     assert fwd_save(lib, s, wsb=need - 1) == DN_ENOWS
     assert fwd_save(lib, s, ws=None) == DN_ENOWS
-    assert fwd_save(lib, shape(chunk=32)) == DN_EUNSUPPORTED
+    assert fwd_save(lib, shape(chunk=32), wsb=need) == DN_ENOWS
     # the backward pass from saved states validates as the recomputing one
     assert bwd_saved(lib, s, g=FAKE, dg=None) == DN_EINVAL
     assert bwd_saved(lib, s, g=None, dg=FAKE) == DN_EINVAL
@@ -243,6 +253,7 @@ def test_bwd_prologue_validation(lib):
     need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
     assert call(wsb=need - 1) == DN_ENOWS
     assert call(dtype_shape=shape(dtype=0)) == DN_EUNSUPPORTED
+    assert call(dtype_shape=shape(chunk=32)) == DN_EUNSUPPORTED  # the folded variants: 64-token chunks
 
 
 def test_bwd_longhorn_validation(lib):
@@ -259,6 +270,7 @@ def test_bwd_longhorn_validation(lib):
     need = lib.dn_chunk_bwd_workspace(ctypes.byref(s))
     assert call(wsb=need - 1) == DN_ENOWS
     assert call(sh=shape(dtype=0)) == DN_EUNSUPPORTED
+    assert call(sh=shape(chunk=32)) == DN_EUNSUPPORTED  # the folded variants: 64-token chunks
 
 
 def test_empty_shape_needs_no_workspace(lib):

@@ -126,11 +126,11 @@ def chunk_grad_bytes(sh) -> float:
     return float(th * per_tok)
 
 
-def chunk_state_bytes(sh) -> float:
+def chunk_state_bytes(sh, chunk=64) -> float:
     """Bytes of the bf16 chunk states h and dh (d_k x d_v per (chunk, head)
     each) that the chunk-gradient kernel reads besides its inputs."""
     lengths = sh.lengths if sh.lengths is not None else [sh.T] * sh.B
-    chunk_heads = sum((L + 63) // 64 for L in lengths) * sh.H
+    chunk_heads = sum((L + chunk - 1) // chunk for L in lengths) * sh.H
     return float(chunk_heads * 2 * sh.Dk * sh.Dv * 2)
 
 
@@ -172,7 +172,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--chunk", type=int, choices=(32, 64), default=64,
-                    help="chunk length of the forward-only workloads (the training pair is 64)")
+                    help="chunk length (the folded prologue and Longhorn backward passes take 64)")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="after the timed steps, this many more steps each preceded by a 1 GiB "
                          "write that evicts the L2s and the 256 MB Infinity Cache; their per-kernel "
@@ -227,7 +227,7 @@ def main():
     ws = None
     if backward:
         ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv, sh.n_seqs,
-                                                sh.dtype), dtype=torch.uint8, device=dev)
+                                                sh.dtype, chunk=args.chunk), dtype=torch.uint8, device=dev)
 
     # every timed step records HIP events on the stream the kernels run on
     # (torch's current stream, which the binding hands to the library)
@@ -242,8 +242,8 @@ def main():
     # event starts the scan, four records per step instead of six
     bev = ([[None, None, mk(), mk()] if saved else [mk() for _ in range(4)] for _ in range(nev)]
            if backward else None)
-    if backward and args.chunk != 64:
-        print("the backward pass runs 64-token chunks only", file=sys.stderr)
+    if backward and args.chunk != 64 and (args.prologue or longhorn):
+        print("the folded prologue and Longhorn backward passes run 64-token chunks only", file=sys.stderr)
         sys.exit(2)
     lev = [(mk(), mk()) for _ in range(nev)]
 
@@ -275,7 +275,8 @@ def main():
             fused = saved and args.prologue and not longhorn
             pro = (d["q_in"], d["k_in"], d["x_in"], d["gate_scale"]) if fused else None
             gr = dn.chunk_bwd(q, k, d["v"], beta, g, d["h0"], d["dO"], d["dhT"],
-                              d["cu_seqlens"], workspace=ws, events=bev[i] if i is not None else None,
+                              d["cu_seqlens"], chunk=args.chunk, workspace=ws,
+                              events=bev[i] if i is not None else None,
                               saved=saved, prologue_inputs=pro,
                               longhorn_beta=b0 if (longhorn and saved) else None)
             if longhorn and not saved:
@@ -346,7 +347,7 @@ def main():
         kname = "dn::fwd_bf16_kernel" if args.chunk == 64 else "dn::fwd32_kernel"
         kus, kbytes = stage_us["fwd"], workload_bytes(sh, False)
     achieved = kbytes / (kus * 1e-6) / 1e9
-    traffic = (CHUNK_GRAD_TRAFFIC_W4 if (backward and wid == 4) else
+    traffic = (CHUNK_GRAD_TRAFFIC_W4 if (backward and wid == 4 and args.chunk == 64) else
                FWD_TRAFFIC_W3 if (wid == 3 and args.chunk == 64 and not args.prologue and not longhorn)
                else None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -357,7 +358,7 @@ def main():
     if traffic is not None:
         roofline["traffic_over_algorithmic"] = round(traffic / kbytes, 3)
     if backward:
-        roofline["chunk_state_bytes"] = chunk_state_bytes(sh)
+        roofline["chunk_state_bytes"] = chunk_state_bytes(sh, args.chunk)
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     out = {
@@ -660,9 +661,9 @@ def bench_chunk_sizes(args, dn, synth, dev):
     """The chunk-size comparison of the DeltaNet rebuttal (answer Q1: forward
     and backward time against the chunk size, at sequence length 4096, batch
     2, head dimension 128, 16 heads), on the ungated delta rule in bf16: the
-    forward pass with 32- and 64-token chunks, and the training pair (the
-    forward pass storing the chunk states, then the backward pass reading
-    them) with 64-token chunks, each timed warm and cold."""
+    forward pass and the training pair (the forward pass storing the chunk
+    states, then the backward pass reading them) with 32- and 64-token
+    chunks, each timed warm and cold."""
     import torch
     sh = synth.Shape(2, 4096, 16, 128, 128, torch.bfloat16, gated=False, has_h0=False, backward=True)
     x = synth.make_inputs(sh, seed=1301)
@@ -675,22 +676,27 @@ def bench_chunk_sizes(args, dn, synth, dev):
         warm, cold = _warm_times(fn, stream), _cold_times(fn, stream)
         res["fwd_C%d" % C] = {"warm_us": round(sum(warm) / len(warm), 2), "cold_median_us": round(med(cold), 2),
                               "cold_min_us": round(min(cold), 2)}
-    ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv), dtype=torch.uint8, device=dev)
+    for C in (32, 64):
+        ws = torch.empty(dn.bwd_workspace_bytes(sh.B, sh.T, sh.H, sh.Dk, sh.Dv, chunk=C), dtype=torch.uint8,
+                         device=dev)
 
-    def train():
-        dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, None, save_workspace=ws)
-        dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], None, None, d["dO"], d["dhT"], workspace=ws, saved=True)
-    warm, cold = _warm_times(train, stream), _cold_times(train, stream)
-    res["fwd+bwd_C64"] = {"warm_us": round(sum(warm) / len(warm), 2), "cold_median_us": round(med(cold), 2),
-                          "cold_min_us": round(min(cold), 2)}
+        def train():
+            dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None, None, chunk=C, save_workspace=ws)
+            dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], None, None, d["dO"], d["dhT"], chunk=C, workspace=ws,
+                         saved=True)
+        warm, cold = _warm_times(train, stream), _cold_times(train, stream)
+        res["fwd+bwd_C%d" % C] = {"warm_us": round(sum(warm) / len(warm), 2),
+                                  "cold_median_us": round(med(cold), 2), "cold_min_us": round(min(cold), 2)}
+        del ws
     th = sh.B * sh.T * sh.H
     res["chunk_state_bytes_C64"] = 2 * (th // 64) * sh.Dk * sh.Dv * 2
     res["chunk_state_bytes_C32"] = 2 * (th // 32) * sh.Dk * sh.Dv * 2
     print(json.dumps({"metric": "chunk-size comparison (DeltaNet rebuttal, answer Q1 setting)",
                       "config": {"workload": "deltanet-B2-T4096-H16-d128-ungated", "dtype": "bf16"},
-                      "results": res, "how": "warm: mean of 20 back-to-back calls; cold: 20 calls each "
-                      "after a 1 GiB write (median, min); chunk_state_bytes: the bf16 states h and dh "
-                      "the training pair stores and reads per chunk size"}), flush=True)
+                      "results": res, "how": "warm: mean of 20 back-to-back calls after untimed calls for "
+                      "%.0f ms of device time; cold: 20 calls each after a 1 GiB write (median, min); "
+                      "chunk_state_bytes: the bf16 states h and dh the training pair stores and reads per "
+                      "chunk size" % WARM_MS}), flush=True)
 
 
 def bench_decode(args, dn, synth, dev):

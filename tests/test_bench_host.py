@@ -22,6 +22,8 @@ def test_chunk_gradient_bytes_per_token_head():
     assert bench.chunk_grad_bytes(synth.WORKLOADS[4]) == 3600 * 4 * 4096 * 16  # 943.7 MB
     assert round(bench.chunk_grad_bytes(synth.WORKLOADS[4]) / 1e6, 1) == 943.7
     assert bench.chunk_state_bytes(synth.WORKLOADS[4]) == 4096 * 2 * 128 * 256 * 2
+    # 32-token chunks: twice the states
+    assert bench.chunk_state_bytes(synth.WORKLOADS[4], 32) == 2 * bench.chunk_state_bytes(synth.WORKLOADS[4])
 
 
 def test_forward_and_decode_floors():

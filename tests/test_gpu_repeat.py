@@ -53,24 +53,25 @@ def test_forward_32_token_chunks_repeats():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("wid", [4, 6])
+@pytest.mark.parametrize("wid,chunk", [(4, 64), (6, 64), (4, 32)])
 @pytest.mark.parametrize("saved", [True, False])
-def test_training_pair_repeats(wid, saved):
+def test_training_pair_repeats(wid, chunk, saved):
     d = to_dev(synth.workload_inputs(wid))
     q, v = d["q"], d["v"]
     N = q.shape[0] if d["cu_seqlens"] is None else d["cu_seqlens"].numel() - 1
-    ws = torch.empty(dn.bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3], v.shape[-1], N),
-                     dtype=torch.uint8, device=DEV)
+    ws = torch.empty(dn.bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3], v.shape[-1], N,
+                                            chunk=chunk), dtype=torch.uint8, device=DEV)
     names = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
     def run():
-        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"],
+        o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"], chunk=chunk,
                              save_workspace=ws if saved else None)
         gr = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
-                          d["cu_seqlens"], workspace=ws, saved=saved)
+                          d["cu_seqlens"], chunk=chunk, workspace=ws, saved=saved)
         return [o, hT] + [gr[n] for n in names]
 
-    assert_repeats(run, f"forward + backward ({'saved states' if saved else 'recompute'}), workload {wid}")
+    assert_repeats(run, f"forward + backward ({'saved states' if saved else 'recompute'}), workload {wid}, "
+                        f"{chunk}-token chunks")
 
 
 def test_decode_repeats():

@@ -36,8 +36,11 @@
  * - Validation happens on the host before any launch; on error nothing is
  *   enqueued.  Kernel faults surface at the caller's next synchronisation.
  * - Supported: Dk in {64, 128}; Dv a positive multiple of 64 up to 1024;
- *   chunk == 64 (dn_chunk_fwd also takes chunk == 32 for DN_BF16 inputs: the
- *   same result with 32-token chunks); dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
+ *   chunk == 64, or 32 for DN_BF16 inputs in dn_chunk_fwd, dn_chunk_fwd_save,
+ *   dn_chunk_bwd, dn_chunk_bwd_events, dn_chunk_bwd_saved and
+ *   dn_chunk_bwd_noalloc (the same result with 32-token chunks: the chunk
+ *   form is an exact refactoring of the token recurrence; the backward
+ *   workspace then holds twice the chunk states); dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
  *   pointers 16-byte aligned; 256 H max(Dk, Dv) < 2^31 (the byte span of one
  *   64-token chunk of fp32 rows, addressed with 32-bit offsets); for the
  *   backward passes, fewer than 2^31 (chunk, head) pairs.  Shapes outside
@@ -70,7 +73,7 @@ typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
 typedef struct {
     int32_t B, T, H, Dk, Dv;
     int32_t n_seqs;
-    int32_t chunk;   /* chunk length: 64 (32 also for the bf16 forward pass) */
+    int32_t chunk;   /* chunk length: 64 (32 also for bf16 inputs, see above) */
     int32_t dtype;   /* dn_dtype of q, k, v, o, dO */
 } dn_shape;
 
@@ -184,8 +187,9 @@ dn_status dn_chunk_bwd_saved(const dn_shape *s,
  * without the fp32 dq, dk, dbeta, dg round trip through HBM.  q, k, beta, g are
  * the prologue's outputs (the recurrence's inputs), q_in and k_in (dtype of q)
  * its raw inputs; the workspace is the one dn_chunk_fwd_save filled.  Errors as
- * dn_chunk_bwd_saved, and DN_EINVAL for null or misaligned q_in, k_in (T > 0)
- * or an x_in/g nullness mismatch.
+ * dn_chunk_bwd_saved, DN_EINVAL for null or misaligned q_in, k_in (T > 0)
+ * or an x_in/g nullness mismatch, and DN_EUNSUPPORTED for chunk == 32 (this
+ * variant runs 64-token chunks only).
  */
 dn_status dn_chunk_bwd_prologue(const dn_shape *s,
                                 const void *q, const void *k, const void *v,
@@ -208,8 +212,8 @@ dn_status dn_chunk_bwd_prologue(const dn_shape *s,
  * deps / (1 + beta |k|^2)^2.  The same values as dn_chunk_bwd_saved followed
  * by dn_longhorn_eps_bwd up to rounding (here (eps / beta)^2 stands for
  * 1 / (1 + beta |k|^2)^2).  The workspace is the one dn_chunk_fwd_save filled
- * with beta := eps.  Errors as dn_chunk_bwd_saved, and DN_EINVAL for a null
- * beta (T > 0).
+ * with beta := eps.  Errors as dn_chunk_bwd_saved, DN_EINVAL for a null
+ * beta (T > 0), and DN_EUNSUPPORTED for chunk == 32 (64-token chunks only).
  */
 dn_status dn_chunk_bwd_longhorn(const dn_shape *s,
                                 const void *q, const void *k, const void *v,

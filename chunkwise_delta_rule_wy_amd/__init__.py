@@ -287,14 +287,14 @@ def chunk_bwd(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, chunk: int = 
     return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dh0=dh0)
 
 
-def chunk_bwd_noalloc(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, out=None):
+def chunk_bwd_noalloc(q, k, v, beta, g, h0, dO, dhT=None, cu_seqlens=None, out=None, chunk: int = 64):
     """``chunk_bwd`` (recomputing) through ``dn_chunk_bwd_noalloc``: the
     library's static scratch buffer replaces the workspace, so the call
     allocates no device memory of its own.  ``out``: optional dict of
     preallocated float32 gradients (dq, dk, dv, dbeta, dg, dh0) to write into;
     missing ones are allocated here.  Returns that dict."""
     lib = load_library()
-    s, N = _shape(q, v, cu_seqlens, 64)
+    s, N = _shape(q, v, cu_seqlens, chunk)
     dev = q.device
     B, T, H, Dk, Dv = s.B, s.T, s.H, s.Dk, s.Dv
     _need(q, "q", q.dtype, (B, T, H, Dk), dev)

@@ -25,18 +25,18 @@ def _dev(x):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
 
 
-def _both(x):
+def _both(x, chunk=64):
     d = _dev(x)
     args = (d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"], d["cu_seqlens"])
-    ref = dn.chunk_bwd(*args)
-    got = dn.chunk_bwd_noalloc(*args)
+    ref = dn.chunk_bwd(*args, chunk=chunk)
+    got = dn.chunk_bwd_noalloc(*args, chunk=chunk)
     torch.cuda.synchronize()
     return ({k: (None if v is None else v.cpu()) for k, v in ref.items()},
             {k: (None if v is None else v.cpu()) for k, v in got.items()})
 
 
-def _check(x, oracle_lib, label):
-    ref, got = _both(x)
+def _check(x, oracle_lib, label, chunk=64):
+    ref, got = _both(x, chunk)
     for name in NAMES:
         if ref[name] is None:
             assert got[name] is None, name
@@ -56,6 +56,16 @@ def test_noalloc_equals_workspace_entry_point_twice(oracle_lib):
     lens = (70, 0, 129, 5)
     small = Shape(1, sum(lens), 3, 128, 256, torch.bfloat16, True, False, backward=True, lengths=lens)
     _check(make_inputs(small, seed=502), oracle_lib, "noalloc call 2")
+
+
+def test_noalloc_32_token_chunks(oracle_lib):
+    # twice the chunk states of 64-token chunks; two calls, the second smaller and packed
+    sh = Shape(1, 1024, 16, 128, 128, torch.bfloat16, True, True, backward=True)
+    assert dn.bwd_workspace_bytes(1, 1024, 16, 128, 128, chunk=32) <= SCRATCH
+    _check(make_inputs(sh, seed=511), oracle_lib, "noalloc C=32 call 1", chunk=32)
+    lens = (31, 0, 33, 65)
+    small = Shape(1, sum(lens), 2, 64, 128, torch.bfloat16, True, True, backward=True, lengths=lens)
+    _check(make_inputs(small, seed=512), oracle_lib, "noalloc C=32 call 2", chunk=32)
 
 
 def test_noalloc_ungated_after_gated(oracle_lib):

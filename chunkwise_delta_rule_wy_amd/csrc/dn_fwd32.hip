@@ -279,15 +279,16 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
     vb[1] = cvt4(vp[1]);
   }
   // O^T = diag(gamma s_c) Y_Q^T + V'^T P^T: lane (n, g) holds O[16nt + n][16w + 4g + e]
+  // the output tiles are stored after the state update (as in the 64-token kernel)
+  bf16x4 obuf[2];
   if constexpr (WRITE_O) {
-    bf16 *orow = static_cast<bf16 *>(p.o) + (row0 * H + h) * (size_t)DV + (col - n) + 4 * g;
     const bf16x8 va = cat(vb[0], vb[1]);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       f32x4 acc = yq[nt];
       if constexpr (GATED) acc = acc * ld<float>(ob + LY::O_CG + CG_GS + 4 * (16 * nt + n));
       acc = mma32(acc, va, ld<bf16x8>(ob + LY::O_P + p_read(lb, nt, 0)));
-      if (16 * nt + n < L) *reinterpret_cast<bf16x4 *>(orow + (size_t)(16 * nt + n) * H * DV) = cvt4(acc);
+      obuf[nt] = cvt4(acc);
     }
   }
   // the state at the chunk start, h = s_c h~, as S = h^T in bf16 (the layout
@@ -323,6 +324,12 @@ __device__ __forceinline__ void chain32(const FwdParams &p, const Bases &lb, f32
     const bf16x4 lo = ld_tr(a);
     const bf16x4 hi = ld_tr(a + 16 * LY::RB);
     hs[mt] = mma32(hs[mt], cat(lo, hi), wb);
+  }
+  if constexpr (WRITE_O) {
+    bf16 *orow = static_cast<bf16 *>(p.o) + (row0 * H + h) * (size_t)DV + (col - n) + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      if (16 * nt + n < L) *reinterpret_cast<bf16x4 *>(orow + (size_t)(16 * nt + n) * H * DV) = obuf[nt];
   }
   mfma_settle();  // the state is read again after the barrier
 }

@@ -31,6 +31,11 @@
 // over Sequence Length" (page 1, answer Q2) with the UT form of the Gated
 // DeltaNet review thread (review 2).
 //
+// 32-token chunks (template argument NB = 2 blocks of 16 tokens instead of
+// 4) use the same organisation on the first half of every token-indexed
+// buffer; the row waves of tokens 32 .. 63 then only issue their share of the
+// tile loads.
+//
 // Organisation.  d_v is walked in 32-column tiles through a two-stage
 // pipeline; in step s
 //   column waves 0..3  take tile s.  Wave 2c ("F") owns tile columns

@@ -23,6 +23,11 @@
 // g, beta two chunks ahead into a three-slot ring.  dh is carried scaled,
 // dh = s dh~, so that the decay costs no work on it (the scale restarts at 1
 // when it would fall below 2^-30), like the forward state.
+//
+// The kernel takes the number NB of 16-token blocks per chunk as a template
+// argument: 4 (64-token chunks) or 2 (32-token chunks, which use the first
+// half of every token-indexed buffer; every product of a block with index
+// >= NB is left out at compile time).
 #include "dn_wy.h"
 
 namespace dn {

@@ -11,6 +11,7 @@
 #include "dn.h"
 
 extern int g_launches;
+extern int g_fail;
 
 static int n_checks = 0;
 
@@ -214,6 +215,25 @@ int main() {
          1);
   EXPECT(dn_short_conv(1, INT32_MAX, 65535, 1024, 4, 1, DN_BF16, P(1), F(2), nullptr, P(3), nullptr),
          DN_EUNSUPPORTED, 0);
+
+  // ---- a failed launch is reported as DN_EHIP, and nothing after it is launched
+  g_fail = 1;
+  s = shape(2, 300, 4, 128, 256, 2, 64, DN_BF16);
+  EXPECT(fwd(&s, nullptr), DN_EHIP, 1);
+  EXPECT(bwd(&s, nullptr, ws), DN_EHIP, 1);  // the recompute fails; the backward kernels are not launched
+  EXPECT(dn_chunk_fwd_save(&s, P(1), P(2), P(3), F(4), F(5), F(6), nullptr, P(20), F(21), P(40), ws, nullptr),
+         DN_EHIP, 1);
+  EXPECT(dn_chunk_bwd_saved(&s, P(1), P(2), P(3), F(4), F(5), F(6), nullptr, P(7), F(8), F(30), F(31), F(32),
+                            F(33), F(34), F(35), P(40), ws, nullptr, nullptr),
+         DN_EHIP, 1);
+  s = shape(1, 300, 4, 128, 256, 5, 64, DN_BF16);
+  EXPECT(bwd(&s, cu, wsv), DN_EHIP, 1);  // the chunk table fails first
+  EXPECT(dn_recurrent_step(256, 32, 128, 128, DN_BF16, P(1), P(2), P(3), F(4), F(5), F(6), P(7), nullptr), DN_EHIP,
+         1);
+  EXPECT(dn_short_conv(2, 100, 4, 128, 4, 2, DN_BF16, P(1), F(2), nullptr, P(3), nullptr), DN_EHIP, 1);
+  EXPECT(dn_prologue(2, 100, 4, 128, DN_BF16, P(1), P(2), F(3), F(4), 0.1f, P(5), P(6), F(7), F(8), nullptr), DN_EHIP,
+         1);
+  g_fail = 0;
 
   printf("abi validation: %d checks passed\n", n_checks);
   return 0;

@@ -2,7 +2,8 @@
 (the forward pass that keeps the chunk states, then the backward pass that
 reads them), against the fp64 oracle, through the C ABI.
 
-The shapes are drawn once from a fixed seed across the supported space:
+The shapes are drawn once from a fixed seed across the supported space (the
+training pair with 64- and 32-token chunks):
 batch, lengths uniform in [1, 320) (so mostly ragged tails), heads, d_k in
 {64, 128}, d_v any multiple of 64 up to 512, every combination of gate and
 initial state, and packed sequences of 2-6 members with lengths uniform in
@@ -56,17 +57,18 @@ def to_dev(x):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
 
 
+@pytest.mark.parametrize("chunk", [64, 32])
 @pytest.mark.parametrize("cfg", CASES, ids=_id)
-def test_random_shape_training_pair(oracle_lib, cfg):
+def test_random_shape_training_pair(oracle_lib, cfg, chunk):
     B, T, H, Dk, Dv, gated, h0, lens = cfg
     sh = Shape(B, T, H, Dk, Dv, torch.bfloat16, gated, h0, backward=True, lengths=lens)
     x = make_inputs(sh, seed=7000 + T + Dv + H)
     d = to_dev(x)
-    ws = torch.empty(dn.bwd_workspace_bytes(B, T, H, Dk, Dv, sh.n_seqs), dtype=torch.uint8, device=DEV)
-    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"],
+    ws = torch.empty(dn.bwd_workspace_bytes(B, T, H, Dk, Dv, sh.n_seqs, chunk=chunk), dtype=torch.uint8, device=DEV)
+    o, hT = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"], chunk=chunk,
                          save_workspace=ws)
     gr = dn.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["dO"], d["dhT"],
-                      d["cu_seqlens"], workspace=ws, saved=True)
+                      d["cu_seqlens"], chunk=chunk, workspace=ws, saved=True)
     torch.cuda.synchronize()
     oo, ho = oracle_lib.fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["cu_seqlens"])
     ref = oracle_lib.bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["h0"], x["dO"], x["dhT"],

@@ -442,17 +442,28 @@ def _settle(fn, stream, warm_ms=WARM_MS):
         fn()
 
 
-def _cold_times(fn, stream, reps=20):
+def _cold_times(fn, stream, reps=20, evict="write"):
     """The cold protocol: untimed calls until the clocks settle, then `reps`
-    calls, each after a 1 GiB write that evicts the L2s and the 256 MB
-    Infinity Cache, timed by events on the launch stream.  Returns the list of
-    times (us)."""
+    calls, each after a 1 GiB pass over a buffer of its own that evicts the
+    L2s and the 256 MB Infinity Cache (reads and writes both allocate there),
+    timed by events on the launch stream.  Returns the list of times (us).
+    evict="write" fills the buffer: the caches then hold the fill's dirty
+    lines, whose write-back the timed call pays for.  evict="read" sums it:
+    the lines left are clean, and the timed call pays for its own traffic
+    only (writes it leaves in the Infinity Cache reach HBM after it)."""
     import torch
-    scratch = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=torch.device("cuda:0"))
+    dev = torch.device("cuda:0")
+    scratch = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    if evict == "read":
+        scratch.fill_(1.0)
     _settle(fn, stream)
     times = []
     for i in range(reps):
-        scratch.fill_(float(i))
+        if evict == "read":
+            torch.sum(scratch, 0, out=sink)
+        else:
+            scratch.fill_(float(i))
         e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         fn()
@@ -487,15 +498,17 @@ def forward_configs(dn, synth, dev, stream):
     res = {}
     med = lambda v: sorted(v)[len(v) // 2]
 
-    def entry(name, nbytes, tokens, warm, cold):
+    def entry(name, nbytes, tokens, warm, cold, cold_rd):
         floor = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
         res[name] = {
             "bytes": nbytes, "floor_us": round(floor, 2),
             "warm_us": {"mean": round(sum(warm) / len(warm), 2), "median": round(med(warm), 2),
                         "min": round(min(warm), 2)},
             "cold_us": {"median": round(med(cold), 2), "min": round(min(cold), 2)},
+            "cold_read_evict_us": {"median": round(med(cold_rd), 2), "min": round(min(cold_rd), 2)},
             "frac_warm": round(floor / (sum(warm) / len(warm)), 4),
             "frac_cold": round(floor / med(cold), 4),
+            "frac_cold_read_evict": round(floor / med(cold_rd), 4),
             "tokens_per_s_cold": round(tokens / (med(cold) * 1e-6), 1),
         }
 
@@ -507,7 +520,8 @@ def forward_configs(dn, synth, dev, stream):
         fn = lambda: dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
         warm = _warm_times(fn, stream)
         cold = _cold_times(fn, stream)
-        entry(synth.WORKLOAD_NAMES[wid], workload_bytes(sh, False), sh.B * sh.T, warm, cold)
+        cold_rd = _cold_times(fn, stream, evict="read")
+        entry(synth.WORKLOAD_NAMES[wid], workload_bytes(sh, False), sh.B * sh.T, warm, cold, cold_rd)
         del d
         torch.cuda.empty_cache()
     x = synth.decode_inputs()
@@ -515,10 +529,13 @@ def forward_configs(dn, synth, dev, stream):
     fn = lambda: dn.recurrent_step(d["q"], d["k"], d["v"], d["beta"], d["g"], d["state"])
     warm = _warm_times(fn, stream)
     cold = _cold_times(fn, stream)
-    entry("decode-B256-H32-d128", decode_bytes(), 256, warm, cold)
+    cold_rd = _cold_times(fn, stream, evict="read")
+    entry("decode-B256-H32-d128", decode_bytes(), 256, warm, cold, cold_rd)
     res["how"] = ("warm: untimed calls for %.0f ms of device time (at least 20), then 20 timed "
                   "back-to-back calls on resident inputs; cold: the same untimed calls, then 20 "
-                  "timed calls each after a 1 GiB write (median, min); " % WARM_MS +
+                  "timed calls each after a 1 GiB write (median, min); cold_read_evict: the same "
+                  "with a 1 GiB read (a sum) in place of the write, which leaves no dirty lines "
+                  "for the timed call to write back; " % WARM_MS +
                   "frac = the HBM floor at 8 TB/s of the algorithmic bytes over the time; "
                   "tokens_per_s_cold counts the decode batch as tokens")
     return res

@@ -40,7 +40,9 @@
  *   dn_chunk_bwd, dn_chunk_bwd_events, dn_chunk_bwd_saved and
  *   dn_chunk_bwd_noalloc (the same result with 32-token chunks: the chunk
  *   form is an exact refactoring of the token recurrence; the backward
- *   workspace then holds twice the chunk states); dtype DN_F32 or DN_BF16 (q, k, v, o, dO share it); all
+ *   workspace then holds twice the chunk states); dtype DN_BF16, or DN_F32
+ *   in dn_chunk_fwd with Dk == 64 and in dn_recurrent_step (q, k, v, o, dO
+ *   share it; every pass that uses the backward workspace is bf16 only); all
  *   pointers 16-byte aligned; 256 H max(Dk, Dv) < 2^31 (the byte span of one
  *   64-token chunk of fp32 rows, addressed with 32-bit offsets); for the
  *   backward passes, fewer than 2^31 (chunk, head) pairs.  Shapes outside
@@ -108,7 +110,8 @@ size_t dn_chunk_bwd_workspace(const dn_shape *s);
  * then runs a reverse sweep for the state gradients and a chunk-parallel pass
  * for the token gradients.  Writes fp32 gradients in the input layouts:
  * dq, dk [B,T,H,Dk], dv [B,T,H,Dv], dbeta [B,T,H], dg [B,T,H] (must be NULL
- * exactly when g is NULL), dh0 [N,H,Dk,Dv] (NULL skips it).
+ * exactly when g is NULL), dh0 [N,H,Dk,Dv] (NULL skips it).  bf16 inputs
+ * only (DN_EUNSUPPORTED for DN_F32).
  */
 dn_status dn_chunk_bwd(const dn_shape *s,
                        const void *q, const void *k, const void *v,

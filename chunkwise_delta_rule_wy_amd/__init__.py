@@ -22,8 +22,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_noalloc", "recurrent_step", "longhorn_eps", "longhorn_eps_bwd", "longhorn_fwd",
-           "longhorn_bwd", "prologue", "prologue_bwd", "DeltaRule", "delta_rule",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_noalloc", "bwd_workspace_bytes", "recurrent_step",
+           "longhorn_eps", "longhorn_eps_bwd", "longhorn_fwd", "longhorn_bwd", "prologue", "prologue_bwd",
+           "short_conv", "short_conv_bwd", "DeltaRule", "delta_rule", "ShortConv", "short_conv_fn",
            "load_library", "LIB_PATH", "DnError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdn.so")

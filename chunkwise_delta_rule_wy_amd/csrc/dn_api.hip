@@ -51,6 +51,15 @@ struct BwdLayout {
   size_t states, dstates, table, total;
 };
 
+// Entries of the longest-first sequence order (packed input of at most
+// MAX_ORDERED_SEQS sequences; larger packs keep their own order).
+size_t order_len(const dn_shape *s, bool varlen) {
+  return varlen && s->n_seqs <= dn::MAX_ORDERED_SEQS ? (size_t)s->n_seqs : 0;
+}
+
+// Backward workspace: bf16 chunk states and state gradients, then for packed
+// input the chunk table (chunk_base [N + 1], chunk_seq [chunks]) and the
+// sequence order [N].
 BwdLayout bwd_layout(const dn_shape *s, bool varlen) {
   BwdLayout L;
   const size_t nch = (size_t)max_chunks(s, varlen);
@@ -58,9 +67,13 @@ BwdLayout bwd_layout(const dn_shape *s, bool varlen) {
   L.states = 0;
   L.dstates = align256(nch * per);
   L.table = L.dstates + align256(nch * per);
-  L.total = L.table + (varlen ? align256(sizeof(int32_t) * ((size_t)s->n_seqs + 1 + nch)) : 0);
+  L.total = L.table +
+            (varlen ? align256(sizeof(int32_t) * ((size_t)s->n_seqs + 1 + nch + order_len(s, varlen))) : 0);
   return L;
 }
+
+// Forward workspace: the sequence order of packed input (nothing otherwise).
+size_t fwd_ws_bytes(const dn_shape *s, bool varlen) { return align256(sizeof(int32_t) * order_len(s, varlen)); }
 
 dn_status from_hip(hipError_t e) { return e == hipSuccess ? DN_OK : DN_EHIP; }
 
@@ -102,7 +115,7 @@ dn_status check_train(const dn_shape *s, const int32_t *cu, const void *q, const
 // (varlen) on `stream`.
 struct TrainWs {
   bf16 *states, *dstates;
-  int32_t *chunk_base, *chunk_seq;
+  int32_t *chunk_base, *chunk_seq, *order;
   int64_t nchunks;
 };
 
@@ -117,13 +130,17 @@ dn_status train_ws(const dn_shape *s, const int32_t *cu, void *workspace, size_t
   // a shape that needs no workspace (no chunk at all) accepts a null one
   if (workspace_bytes < L.total || (L.total > 0 && (!workspace || !aligned16(workspace)))) return DN_ENOWS;
   char *ws = static_cast<char *>(workspace);
-  w.chunk_base = w.chunk_seq = nullptr;
+  w.chunk_base = w.chunk_seq = w.order = nullptr;
   if (varlen) {
     w.chunk_base = reinterpret_cast<int32_t *>(ws + L.table);
     w.chunk_seq = w.chunk_base + s->n_seqs + 1;
     hipError_t e = dn::launch_chunk_table(cu, s->n_seqs, w.chunk_base, w.chunk_seq, (int)w.nchunks, chunk_len(s),
                                           stream);
     if (e != hipSuccess) return DN_EHIP;
+    if (order_len(s, true) > 0) {
+      w.order = w.chunk_seq + w.nchunks;
+      if (dn::launch_seq_order(cu, s->n_seqs, w.order, stream) != hipSuccess) return DN_EHIP;
+    }
   }
   w.states = reinterpret_cast<bf16 *>(ws + L.states);
   w.dstates = reinterpret_cast<bf16 *>(ws + L.dstates);
@@ -180,6 +197,7 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   dn::FwdParams fp = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
   fp.states = w.states;
   fp.chunk_base = w.chunk_base;
+  fp.seq_order = w.order;
   if (recompute) {
     hipError_t e = s->chunk == 32 ? dn::launch_fwd_c32(fp, s->Dk, true, false, stream)
                                   : dn::launch_fwd(fp, s->dtype, s->Dk, true, false, stream);
@@ -199,6 +217,7 @@ dn_status bwd_run(const dn_shape *s, const void *q, const void *k, const void *v
   bp.cu = cu_seqlens;
   bp.chunk_base = w.chunk_base;
   bp.chunk_seq = w.chunk_seq;
+  bp.seq_order = w.order;
   bp.states = w.states;
   bp.dstates = w.dstates;
   bp.dq = dq;
@@ -256,8 +275,8 @@ const char *dn_status_str(dn_status s) {
 }
 
 size_t dn_chunk_fwd_workspace(const dn_shape *s) {
-  (void)s;
-  return 0;
+  if (!s || s->B <= 0 || s->n_seqs <= 0) return 0;
+  return fwd_ws_bytes(s, s->n_seqs != s->B || s->B == 1);
 }
 
 dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const void *v,
@@ -266,15 +285,20 @@ dn_status dn_chunk_fwd(const dn_shape *s, const void *q, const void *k, const vo
                        size_t workspace_bytes, hipStream_t stream) {
   dn_status st = check_shape(s, cu_seqlens, true);
   if (st != DN_OK) return st;
-  (void)workspace;
-  (void)workspace_bytes;
   if (s->T > 0) {
     if (!q || !k || !v || !beta || !o) return DN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return DN_EINVAL;
   }
+  const size_t need = cu_seqlens ? fwd_ws_bytes(s, true) : 0;
+  if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace))) return DN_ENOWS;
   dn::FwdParams p = fwd_params(s, q, k, v, beta, g, h0, cu_seqlens);
   p.o = o;
   p.hT = hT;
+  if (need > 0) {
+    int32_t *order = static_cast<int32_t *>(workspace);
+    if (dn::launch_seq_order(cu_seqlens, s->n_seqs, order, stream) != hipSuccess) return DN_EHIP;
+    p.seq_order = order;
+  }
   if (s->chunk == 32) return from_hip(dn::launch_fwd_c32(p, s->Dk, false, true, stream));
   return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, false, true, stream));
 }
@@ -319,6 +343,7 @@ dn_status dn_chunk_fwd_save(const dn_shape *s, const void *q, const void *k, con
   p.hT = hT;
   p.states = w.states;
   p.chunk_base = w.chunk_base;
+  p.seq_order = w.order;
   if (s->chunk == 32) return from_hip(dn::launch_fwd_c32(p, s->Dk, true, true, stream));
   return from_hip(dn::launch_fwd(p, s->dtype, s->Dk, true, true, stream));
 }

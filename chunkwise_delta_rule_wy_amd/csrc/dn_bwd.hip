@@ -19,6 +19,11 @@
 //    every d_v column computes dq, dk, dv, dbeta and dg from the chunk's
 //    inputs, the stored state h_c and the stored dh.
 //
+// For packed input this file also builds the two tables in the workspace that
+// the passes read: the chunk table (the global chunks of every sequence) and
+// the order of the sequences, longest first, in which the sequential passes
+// hand them to workgroups.
+//
 // States and state gradients are stored in bf16, transposed (S = h^T,
 // [chunk][H][d_v][d_k]): each lane writes the bf16 fragment it feeds its own
 // MFMAs with, and the chunk kernel loads them directly into LDS.
@@ -82,6 +87,40 @@ hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int
                               int max_chunks, int chunk, hipStream_t stream) {
   hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(TABLE_THREADS), 0, stream, cu, N, chunk_base, chunk_seq,
                      max_chunks, chunk);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ sequence order
+// order[r] is the sequence with the r-th most tokens, ties broken by the lower
+// index: the rank of sequence n is the number of sequences that come before it
+// in that total order, so the ranks are a permutation of 0 .. N - 1.  Thread n
+// ranks sequence n against every length, read through LDS in tiles that all
+// threads of the workgroup scan in step (broadcast reads).
+constexpr int ORDER_THREADS = 256;
+constexpr int ORDER_TILE = 2048;
+
+__global__ __launch_bounds__(ORDER_THREADS) void seq_order_kernel(const int32_t *cu, int N, int32_t *order) {
+  __shared__ int lens[ORDER_TILE];
+  const int n = blockIdx.x * ORDER_THREADS + threadIdx.x;
+  const int len_n = n < N ? cu[n + 1] - cu[n] : 0;
+  int rank = 0;
+  for (int m0 = 0; m0 < N; m0 += ORDER_TILE) {
+    const int cnt = min(ORDER_TILE, N - m0);
+    __syncthreads();  // the previous tile is no longer read
+    for (int i = threadIdx.x; i < cnt; i += ORDER_THREADS) lens[i] = cu[m0 + i + 1] - cu[m0 + i];
+    __syncthreads();
+    for (int i = 0; i < cnt; ++i) {
+      const int lm = lens[i];
+      rank += (lm > len_n) || (lm == len_n && m0 + i < n);
+    }
+  }
+  if (n < N) order[rank] = n;
+}
+
+hipError_t launch_seq_order(const int32_t *cu, int N, int32_t *order, hipStream_t stream) {
+  if (N <= 0 || N > MAX_ORDERED_SEQS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(seq_order_kernel, dim3((N + ORDER_THREADS - 1) / ORDER_THREADS), dim3(ORDER_THREADS), 0, stream,
+                     cu, N, order);
   return hipGetLastError();
 }
 

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(F32_THREADS, 1) void fwd32_kernel(FwdParams p) {
   int pair, tile;
   wg_coords(blockIdx.x, p.ntiles, p.xcd_map, pair, tile);
   if (pair >= p.N * p.H) return;
-  const int n_seq = pair / p.H, h = pair % p.H;
+  const int n_seq = pair_seq(p.seq_order, pair / p.H), h = pair % p.H;
   const int dv0 = tile * DVT;
   const SeqInfo si = seq_info(p.cu, n_seq, p.T);
   const int nch = (si.len + C32 - 1) / C32;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
   int pair, tile;
   wg_coords(blockIdx.x, p.ntiles, p.xcd_map, pair, tile);
   if (pair >= p.N * p.H) return;
-  const int n_seq = pair / p.H, h = pair % p.H;
+  const int n_seq = pair_seq(p.seq_order, pair / p.H), h = pair % p.H;
   const int dv0 = tile * DVT;
   const SeqInfo si = seq_info(p.cu, n_seq, p.T);
   const int nch = (si.len + CH - 1) / CH;

@@ -17,6 +17,7 @@ struct FwdParams {
   float *hT;                  // may be null
   bf16 *states;               // chunk-start states S = h^T, bf16 [chunk][H][DV][DK] (backward only)
   const int32_t *chunk_base;  // varlen: first global chunk of each sequence (backward only)
+  const int32_t *seq_order;   // varlen: the sequences longest first, or null (their own order)
   int B, T, H, DV, N, NC;     // NC: chunks per sequence for fixed length
   int ntiles;                 // DV / 64
   int xcd_map;                // 1 when (N * H) % 8 == 0
@@ -28,6 +29,7 @@ struct BwdParams {
   const int32_t *cu;
   const int32_t *chunk_base;  // varlen: first global chunk of each sequence
   const int32_t *chunk_seq;   // varlen: sequence of each global chunk
+  const int32_t *seq_order;   // varlen: the sequences longest first, or null (their own order)
   const bf16 *states;         // chunk-start states S = h^T, bf16 [chunk][H][DV][DK]
   bf16 *dstates;              // gradient w.r.t. each chunk's end state, same layout
   float *dq, *dk, *dv, *dbeta, *dg, *dh0;
@@ -124,6 +126,12 @@ __device__ __forceinline__ void wg_coords(int x, int ntiles, int xcd_map, int &p
   }
 }
 
+// Sequence of the pair rank r (pair index / H).  Packed input with an order
+// table walks the sequences longest first: the workgroups of the longest
+// sequence, whose chunk chain is the pass's critical path, then start in the
+// first wave of workgroups instead of waiting for a CU.
+__device__ __forceinline__ int pair_seq(const int32_t *order, int r) { return order ? order[r] : r; }
+
 size_t fwd_smem_bytes(int dtype, int DK);
 size_t fwd_ref_smem_bytes(int dtype, int DK);
 hipError_t launch_fwd(const FwdParams &p, int dtype, int DK, bool store_states, bool write_o,
@@ -139,6 +147,10 @@ hipError_t launch_prologue(const PrologueParams &p, int dtype, int DK, bool back
 hipError_t launch_conv(const ConvParams &p, int dtype, bool backward, hipStream_t stream);
 hipError_t launch_chunk_table(const int32_t *cu, int N, int32_t *chunk_base, int32_t *chunk_seq,
                               int max_chunks, int chunk, hipStream_t stream);
+// order[r] = the sequence with the r-th most tokens (ties: the lower index
+// first), for N <= MAX_ORDERED_SEQS sequences
+constexpr int MAX_ORDERED_SEQS = 65536;
+hipError_t launch_seq_order(const int32_t *cu, int N, int32_t *order, hipStream_t stream);
 // ev_scan / ev_chunk (may be null) are recorded on `stream` after the scan and
 // after the chunk-gradient kernel
 hipError_t launch_bwd(const BwdParams &p, int dtype, int DK, hipStream_t stream, hipEvent_t ev_scan = nullptr,

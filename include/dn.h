@@ -33,6 +33,11 @@
  *   covers tokens [cu[n], cu[n+1]) and chunks restart at every sequence start.
  *   A zero-length sequence passes its h0 through to hT.  The library does not
  *   copy cu_seqlens to the host; malformed offsets are undefined behaviour.
+ *   The sequential passes take packed sequences longest first: a small kernel
+ *   ranks them by length into the workspace, so that the longest sequence,
+ *   whose chain of chunks is the critical path, starts in the first wave of
+ *   workgroups wherever it sits in the pack (packs of more than 65536
+ *   sequences keep their own order).  The results do not depend on it.
  * - Validation happens on the host before any launch; on error nothing is
  *   enqueued.  Kernel faults surface at the caller's next synchronisation.
  * - Supported: Dk in {64, 128}; Dv a positive multiple of 64 up to 1024;
@@ -82,7 +87,10 @@ typedef struct {
 /* Human-readable name of a status code (static string). */
 const char *dn_status_str(dn_status s);
 
-/* Bytes of device workspace dn_chunk_fwd needs for this shape (may be 0). */
+/* Bytes of device workspace dn_chunk_fwd needs for this shape: for packed
+ * input (the query assumes it when B == 1 or n_seqs != B) 4 bytes per
+ * sequence, rounded up to 256, for the order in which the pass takes the
+ * sequences; 0 otherwise (then workspace may be NULL). */
 size_t dn_chunk_fwd_workspace(const dn_shape *s);
 
 /*
@@ -92,6 +100,9 @@ size_t dn_chunk_fwd_workspace(const dn_shape *s);
  * chunk-start states stay on chip; nothing but o and hT is written
  * (Parallelizing Linear Transformers..., page 1, answer Q2, describes the
  * materialise-then-recompute trade-off this pass avoids for inference).
+ * With cu_seqlens the workspace (16-byte aligned) must hold
+ * dn_chunk_fwd_workspace(s) bytes (DN_ENOWS otherwise); the call writes the
+ * sequence order there.
  */
 dn_status dn_chunk_fwd(const dn_shape *s,
                        const void *q, const void *k, const void *v,

@@ -36,8 +36,8 @@ static dn_shape shape(int B, int T, int H, int Dk, int Dv, int N, int chunk, int
   return s;
 }
 
-static dn_status fwd(const dn_shape *s, const int32_t *cu, void *o = P(20)) {
-  return dn_chunk_fwd(s, P(1), P(2), P(3), F(4), F(5), F(6), cu, o, F(21), nullptr, 0, nullptr);
+static dn_status fwd(const dn_shape *s, const int32_t *cu, void *o = P(20), void *ws = nullptr, size_t wsb = 0) {
+  return dn_chunk_fwd(s, P(1), P(2), P(3), F(4), F(5), F(6), cu, o, F(21), ws, wsb, nullptr);
 }
 
 static dn_status bwd(const dn_shape *s, const int32_t *cu, size_t ws, const float *g = F(5), float *dg = F(34),
@@ -81,6 +81,18 @@ int main() {
   s = shape(2, 10, 4, 128, 128, 3, 64, DN_BF16);
   EXPECT(fwd(&s, cu), DN_EINVAL, 0);       // offsets need B == 1
   s = shape(1, 10, 4, 128, 128, 3, 64, DN_BF16);
+  // packed input: the workspace holds the longest-first sequence order (3 entries, one 256-byte block)
+  if (dn_chunk_fwd_workspace(&s) != 256) return 1;
+  EXPECT(fwd(&s, cu), DN_ENOWS, 0);
+  EXPECT(fwd(&s, cu, P(20), P(41), 255), DN_ENOWS, 0);
+  EXPECT(fwd(&s, cu, P(20), reinterpret_cast<char *>(P(41)) + 4, 256), DN_ENOWS, 0);  // misaligned
+  EXPECT(fwd(&s, cu, P(20), P(41), 256), DN_OK, 2);  // the order, then the forward kernel
+  s.chunk = 32;
+  EXPECT(fwd(&s, cu, P(20), P(41), 256), DN_OK, 2);
+  s = shape(2, 10, 4, 128, 128, 2, 64, DN_BF16);
+  if (dn_chunk_fwd_workspace(&s) != 0) return 1;  // fixed-length input needs none
+  s = shape(1, 10, 4, 128, 128, 70000, 64, DN_BF16);
+  if (dn_chunk_fwd_workspace(&s) != 0) return 1;  // packs above 65536 sequences keep their own order
   EXPECT(fwd(&s, cu), DN_OK, 1);
   s = shape(1, 10, 4, 128, 128, 1, 64, 7);
   EXPECT(fwd(&s, nullptr), DN_EINVAL, 0);
@@ -121,7 +133,7 @@ int main() {
   EXPECT(bwd(&s, nullptr, ws), DN_EUNSUPPORTED, 0);
   s = shape(1, 300, 4, 128, 256, 5, 64, DN_BF16);
   const size_t wsv = dn_chunk_bwd_workspace(&s);
-  EXPECT(bwd(&s, cu, wsv), DN_OK, 3);          // chunk table, recompute, backward
+  EXPECT(bwd(&s, cu, wsv), DN_OK, 4);          // chunk table, sequence order, recompute, backward
   EXPECT(bwd(&s, cu, wsv - 1), DN_ENOWS, 0);
   s = shape(1, 0, 4, 128, 256, 3, 64, DN_BF16);
   EXPECT(dn_chunk_bwd(&s, nullptr, nullptr, nullptr, nullptr, F(5), F(6), cu, nullptr, F(8), nullptr, nullptr,
@@ -129,7 +141,7 @@ int main() {
          DN_ENOWS, 0);  // packed, all empty: the workspace still holds the chunk table
   EXPECT(dn_chunk_bwd(&s, nullptr, nullptr, nullptr, nullptr, F(5), F(6), cu, nullptr, F(8), nullptr, nullptr,
                       nullptr, nullptr, F(34), F(35), P(40), dn_chunk_bwd_workspace(&s), nullptr),
-         DN_OK, 3);
+         DN_OK, 4);
   if (dn_chunk_bwd_workspace(nullptr) != 0) return 1;
   s = shape(1, INT32_MAX, 1 << 12, 128, 1024, 1, 64, DN_BF16);
   EXPECT(bwd(&s, nullptr, (size_t)-1), DN_EUNSUPPORTED, 0);  // too many (chunk, head) pairs
@@ -178,7 +190,7 @@ int main() {
                                F(32), F(33), F(34), F(35), P(40), ws32, nullptr, nullptr),
          DN_EUNSUPPORTED, 0);
   s = shape(1, 300, 4, 128, 256, 5, 32, DN_BF16);
-  EXPECT(bwd(&s, cu, dn_chunk_bwd_workspace(&s)), DN_OK, 3);  // chunk table, recompute, backward
+  EXPECT(bwd(&s, cu, dn_chunk_bwd_workspace(&s)), DN_OK, 4);  // chunk table, order, recompute, backward
 
   // ---- decode step
   EXPECT(dn_recurrent_step(256, 32, 128, 128, DN_BF16, P(1), P(2), P(3), F(4), F(5), F(6), P(7), nullptr), DN_OK,
@@ -228,6 +240,8 @@ int main() {
          DN_EHIP, 1);
   s = shape(1, 300, 4, 128, 256, 5, 64, DN_BF16);
   EXPECT(bwd(&s, cu, wsv), DN_EHIP, 1);  // the chunk table fails first
+  s = shape(1, 10, 4, 128, 128, 3, 64, DN_BF16);
+  EXPECT(fwd(&s, cu, P(20), P(41), 256), DN_EHIP, 1);  // the order fails; the forward is not launched
   EXPECT(dn_recurrent_step(256, 32, 128, 128, DN_BF16, P(1), P(2), P(3), F(4), F(5), F(6), P(7), nullptr), DN_EHIP,
          1);
   EXPECT(dn_short_conv(2, 100, 4, 128, 4, 2, DN_BF16, P(1), F(2), nullptr, P(3), nullptr), DN_EHIP, 1);

@@ -28,6 +28,7 @@ hipError_t launch_conv(const ConvParams &, int, bool, hipStream_t) { return laun
 hipError_t launch_chunk_table(const int32_t *, int, int32_t *, int32_t *, int, int, hipStream_t) {
   return launched();
 }
+hipError_t launch_seq_order(const int32_t *, int, int32_t *, hipStream_t) { return launched(); }
 hipError_t launch_bwd(const BwdParams &, int, int, hipStream_t, hipEvent_t, hipEvent_t) { return launched(); }
 hipError_t launch_bwd_scan(const BwdParams &, int, hipStream_t) { return launched(); }
 hipError_t launch_bwd_chunk(const BwdParams &, int, hipStream_t) { return launched(); }

@@ -104,6 +104,31 @@ def test_fwd_rejects_null_and_misaligned(lib):
     assert fwd(lib, shape(B=2, n_seqs=3), cu=FAKE) == DN_EINVAL
 
 
+def test_fwd_workspace_holds_the_sequence_order(lib):
+    # packed input: 4 bytes per sequence (the longest-first order), rounded to 256
+    s = shape(B=1, T=1000, n_seqs=7)
+    assert lib.dn_chunk_fwd_workspace(ctypes.byref(s)) == 256
+    assert lib.dn_chunk_fwd_workspace(ctypes.byref(shape(B=1, T=10 ** 6, n_seqs=65536))) == 4 * 65536
+    assert lib.dn_chunk_fwd_workspace(ctypes.byref(shape(B=1, T=10 ** 6, n_seqs=65537))) == 0  # own order
+    assert lib.dn_chunk_fwd_workspace(ctypes.byref(shape())) == 0  # fixed length: none
+    P = ctypes.c_void_p
+
+    def call(ws, wsb):
+        return lib.dn_chunk_fwd(ctypes.byref(s), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, P(FAKE),
+                                P(FAKE), None, P(ws) if ws else None, wsb, None)
+    assert call(None, 0) == DN_ENOWS
+    assert call(FAKE, 255) == DN_ENOWS
+    assert call(FAKE + 4, 256) == DN_ENOWS  # misaligned
+    # the backward workspace: bf16 states and state gradients for at most
+    # T/64 + n_seqs chunks, then chunk_base [N + 1], chunk_seq [chunks] and the
+    # order [N] as int32 (each part rounded up to 256 bytes)
+    nch, per = 1000 // 64 + 7, 2 * 64 * 64 * 2
+    assert lib.dn_chunk_bwd_workspace(ctypes.byref(s)) == 2 * nch * per + 256 * -(-4 * (8 + nch + 7) // 256)
+    big = shape(B=1, T=64 * 1000, n_seqs=1000)
+    nch = 2000
+    assert lib.dn_chunk_bwd_workspace(ctypes.byref(big)) == 2 * nch * per + 256 * -(-4 * (1001 + nch + 1000) // 256)
+
+
 def test_bwd_validation(lib):
     s = shape()
     assert bwd(lib, s, g=FAKE, dg=None) == DN_EINVAL

@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 # FETCH_SIZE and WRITE_SIZE scaled by what the same counters read for a copy of
 # known size (commands and raw counts under profiles/); it describes the kernel as
 # built when the counters were taken
-CHUNK_GRAD_TRAFFIC_W4 = 1511.2e6
+CHUNK_GRAD_TRAFFIC_W4 = 1511.4e6
 # the same for the forward kernel at the gated forward-only workload (B=4 T=4096
 # H=16 dk=128 dv=256): 294.0 MB read + 142.6 MB written
 FWD_TRAFFIC_W3 = 436.6e6

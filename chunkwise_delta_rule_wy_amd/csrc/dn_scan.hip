@@ -114,6 +114,51 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
 #pragma unroll
     for (int kb = t >> 1; kb < NKB; ++kb) dvp[t] = mma32(dvp[t], ld<bf16x8>(ob + RS::O_P + pt_frag(t, kb, l)), dob[kb]);
 
+  // dh~ <- dh~ + Q^T diag(gamma / s) dO - K^T diag(gamma / s) dX (after dh~ *= gamma_63 s on a restart):
+  // the restart scale and the dO term first (neither depends on dX), the dX term after the substitution;
+  // contraction slot 8g + s of block kb is token 32kb + 16(s/4) + 4g + s%4
+  if constexpr (GATED) {
+    const float hsc = ld<float>(cgt + CG_HSCALE);
+    if (hsc != 1.f) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) hs[mt] = hs[mt] * hsc;
+    }
+    __asm__ volatile("s_nop 4" ::: "memory");
+  }
+  {
+    bf16x8 bo[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      bf16x4 part[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x4 d = ld_tr(slot + LY::S_D + 32 * kb * 128 + dpr[hh]);
+        if constexpr (GATED) {
+          const f32x4 gs = ld<f32x4>(cgt + CG_GS + 4 * (32 * kb + 16 * hh + 4 * g));
+          f32x4 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = bf2f(d[e]) * gs[e];
+          part[hh] = cvt4(f);
+        } else {
+          part[hh] = d;
+        }
+      }
+      bo[kb] = cat(part[0], part[1]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = hs[mt];
+      const uint32_t aoff = 8 * (mt & 1) + (lb.ktr ^ (64 * (mt >> 1)));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t r0 = 32 * kb * LY::RB, r1 = (32 * kb + 16) * LY::RB;
+        const bf16x8 qt = cat(ld_tr(slot + LY::S_Q + aoff + r0), ld_tr(slot + LY::S_Q + aoff + r1));
+        acc = mma32(acc, qt, bo[kb]);
+      }
+      hs[mt] = acc;
+    }
+  }
+
   // dX_i = diag(beta_i) R_ii^T (dV'_i - sum_{m>i} M_mi^T dX_m)
   f32x4 dx[NB];
   bf16x4 dxb[NB];
@@ -126,41 +171,15 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
     dx[i] = y * ld<f32x4>(slot + LY::S_BETA + 4 * (16 * i + 4 * g));
     dxb[i] = cvt4(dx[i]);
   }
-
-  // dh~ <- dh~ + Q^T diag(gamma / s) dO - K^T diag(gamma / s) dX (after dh~ *= gamma_63 s on a restart);
-  // contraction slot 8g + s of block kb is token 32kb + 16(s/4) + 4g + s%4
-  bf16x8 bo[NKB], bx[NKB];
+  bf16x8 bx[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    bf16x4 part[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16x4 d = ld_tr(slot + LY::S_D + 32 * kb * 128 + dpr[hh]);
-      if constexpr (GATED) {
-        const f32x4 gs = ld<f32x4>(cgt + CG_GS + 4 * (32 * kb + 16 * hh + 4 * g));
-        f32x4 f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = bf2f(d[e]) * gs[e];
-        part[hh] = cvt4(f);
-      } else {
-        part[hh] = d;
-      }
-    }
-    bo[kb] = cat(part[0], part[1]);
     f32x4 x0 = -dx[2 * kb], x1 = -dx[2 * kb + 1];
     if constexpr (GATED) {
       x0 = x0 * ld<f32x4>(cgt + CG_GS + 4 * (32 * kb + 4 * g));
       x1 = x1 * ld<f32x4>(cgt + CG_GS + 4 * (32 * kb + 16 + 4 * g));
     }
     bx[kb] = cat(cvt4(x0), cvt4(x1));
-  }
-  if constexpr (GATED) {
-    const float hsc = ld<float>(cgt + CG_HSCALE);
-    if (hsc != 1.f) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) hs[mt] = hs[mt] * hsc;
-    }
-    __asm__ volatile("s_nop 4" ::: "memory");
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -169,9 +188,7 @@ __device__ __forceinline__ void chain_chunk(const Bases &lb, f32x4 (&hs)[DK / 16
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const uint32_t r0 = 32 * kb * LY::RB, r1 = (32 * kb + 16) * LY::RB;
-      const bf16x8 qt = cat(ld_tr(slot + LY::S_Q + aoff + r0), ld_tr(slot + LY::S_Q + aoff + r1));
       const bf16x8 kt = cat(ld_tr(slot + LY::S_K + aoff + r0), ld_tr(slot + LY::S_K + aoff + r1));
-      acc = mma32(acc, qt, bo[kb]);
       acc = mma32(acc, kt, bx[kb]);
     }
     hs[mt] = acc;

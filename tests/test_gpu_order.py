@@ -74,3 +74,33 @@ def test_permuted_pack_permutes_every_output(mode, chunk):
                 b = t[:, cu[j]:cu[j + 1]]
                 assert torch.equal(a, b), (name, perm, i, j)
     print("mode %s, chunk %d: three permutations bit-identical" % (mode, chunk), flush=True)
+
+
+@pytest.mark.parametrize("lens", [LENS, (5, 5, 0, 5, 64, 1, 64, 3), tuple(range(300, 0, -1)) + (0, 1000),
+                                  tuple((7 * i) % 13 for i in range(2500))],  # several LDS tiles of lengths
+                         ids=["pack", "ties", "302seqs", "2500seqs"])
+def test_order_table_is_longest_first(lens):
+    """dn_chunk_fwd leaves the order in the caller's workspace: the sequences
+    by length, longest first, ties by index (checked through the C ABI)."""
+    import ctypes
+    h, dk, dv = 2, 64, 64
+    sh = Shape(1, sum(lens), h, dk, dv, torch.bfloat16, True, True, lengths=lens)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in make_inputs(sh, seed=17).items()}
+    lib = dn.load_library()
+    s = dn._Shape(1, sum(lens), h, dk, dv, len(lens), 64, dn.DN_BF16)
+    need = lib.dn_chunk_fwd_workspace(ctypes.byref(s))
+    assert need >= 4 * len(lens)
+    ws = torch.full((need // 4,), -1, dtype=torch.int32, device=DEV)
+    o = torch.empty_like(d["v"])
+    hT = torch.empty_like(d["h0"])
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.dn_chunk_fwd(ctypes.byref(s), P(d["q"]), P(d["k"]), P(d["v"]), P(d["beta"]), P(d["g"]), P(d["h0"]),
+                          P(d["cu_seqlens"]), P(o), P(hT), P(ws), need,
+                          ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    want = sorted(range(len(lens)), key=lambda i: (-lens[i], i))
+    assert ws[:len(lens)].cpu().tolist() == want
+    # and the outputs are those of the library's own call
+    o2, hT2 = dn.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["cu_seqlens"])
+    assert torch.equal(o, o2) and torch.equal(hT, hT2)

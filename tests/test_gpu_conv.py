@@ -8,7 +8,7 @@ when y is stored in bf16; dx within 1e-6; dw, a sum over every token in
 fp32, within 1e-5.  Cases span several 32-token runs and 512-channel groups
 with ragged tails, packed sequences with empty and one-token members, every
 width 1..4, and the training shapes (B=4 T=4096 H=16 d=128, and the packed
-65536-token, H=32 input) with the oracle on sampled heads.  The variant fused
+65536-token, H=32 input) on every head.  The variant fused
 with the per-head L2 normalisation is compared with the oracle's convolution
 followed by its prologue normalisation, and a whole layer (projections through
 the convolutions, the chunkwise passes and back) with the oracle's composition.

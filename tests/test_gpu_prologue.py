@@ -4,8 +4,9 @@ g = -c softplus) and its backward against the fp64 oracle, through the C ABI.
 Both are plain fp32 arithmetic on exactly upcast inputs: fp32 outputs within
 1e-5 relative of the oracle, bf16 outputs (q, k) within one bf16 rounding
 (2^-8 relative).  The composed path (prologue, chunkwise forward and
-backward, prologue backward) is checked at the benchmark's shape on sampled
-(batch, head) pairs within relative L2 2e-2, like the recurrence alone.
+backward, prologue backward) is checked at the benchmark's shape on every
+(batch, head) pair and every chunk within relative L2 2e-2, like the
+recurrence alone.
 """
 import numpy as np
 import pytest

@@ -35,12 +35,9 @@ def run(x, w, dy, cu):
     return y.cpu(), dx.cpu(), dw.cpu()
 
 
-def check(oracle_lib, inp, heads=None):
+def check(oracle_lib, inp):
     x, w, dy, cu = inp["x"], inp["w"], inp["dy"], inp["cu_seqlens"]
     y, dx, dw = run(x, w, dy, cu)
-    if heads is not None:  # every channel is independent: the oracle on a few heads
-        x, w, dy = x[:, :, heads], w[heads], dy[:, :, heads]
-        y, dx, dw = y[:, :, heads], dx[:, :, heads], dw[heads]
     ry = oracle_lib.short_conv(x, w, cu)
     rdx, rdw = oracle_lib.short_conv_bwd(x, w, dy, cu)
     # y and dx over the whole tensor, every (sequence, head) pair and every chunk
@@ -123,16 +120,13 @@ def l2_reference(oracle_lib, x, w, dy, cu):
     return y, dx, dw
 
 
-def check_l2(oracle_lib, inp, heads=None):
+def check_l2(oracle_lib, inp):
     x, w, dy, cu = inp["x"], inp["w"], inp["dy"], inp["cu_seqlens"]
     d = lambda t: None if t is None else t.to(DEV)
     y = dn.short_conv(d(x), d(w), d(cu), l2norm=True)
     dx, dw = dn.short_conv_bwd(d(x), d(w), d(dy), d(cu), l2norm=True)
     torch.cuda.synchronize()
     y, dx, dw = y.cpu(), dx.cpu(), dw.cpu()
-    if heads is not None:
-        x, w, dy = x[:, :, heads], w[heads], dy[:, :, heads]
-        y, dx, dw = y[:, :, heads], dx[:, :, heads], dw[heads]
     ry, rdx, rdw = l2_reference(oracle_lib, x, w, dy, cu)
     parity.check("y", parity.token_errors(y, ry, cu), YTOL[x.dtype], "conv l2")
     parity.check("dx", parity.token_errors(dx, rdx, cu), 1e-5, "conv l2")

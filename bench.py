@@ -140,6 +140,12 @@ def decode_bytes(B=256, H=32, Dk=128, Dv=128) -> float:
     return float(B * H * Dk * Dv * 4 * 2 + B * H * (2 * Dk + 2 * Dv) * 2 + B * H * 8)
 
 
+def decode_flops(B=256, H=32, Dk=128, Dv=128) -> float:
+    """Algorithmic flops of one decode step: per state, the two matrix-vector
+    products h^T k and h^T q and the rank-one update, 2 d_k d_v MACs each."""
+    return 2.0 * 3 * Dk * Dv * B * H
+
+
 def bwd_flops(sh) -> float:
     """Algorithmic flops of the backward pass without the recompute, per
     token-head (MACs): 6 dk dv for the state products, (C+1)/2 (5 dk + 4 dv)
@@ -151,12 +157,16 @@ def bwd_flops(sh) -> float:
 
 
 def fwd_flops(sh) -> float:
-    """Algorithmic flops of the chunkwise forward pass as this library
-    evaluates it (triangular products at their exact half), per token-head:
-    K K^T strict (C-1)/2 dk, Q K^T (C+1)/2 dk, (I+A)^-1 C^2/6,
-    T X and P V' (C+1)/2 dv each, K h, Q h, K^T V' dk dv each (MACs)."""
+    """Algorithmic flops of the chunkwise forward pass per token-head (MACs,
+    triangular products at their exact half): K K^T strict (C-1)/2 d_k; the
+    causal products Q K^T and T diag(gamma) K, (C+1)/2 d_k each, and T V and
+    P V', (C+1)/2 d_v each; the state products K h, Q h and K^T V', d_k d_v
+    each; the inverse of (I + A), C^2/6.  This is the method's count, with the
+    WY factors W = T diag(gamma) K and U = T V formed; the library applies T to
+    V - diag(gamma) K h instead and does fewer flops than it is credited with
+    (the d_k term of the T product)."""
     C, dk, dv = 64, sh.Dk, sh.Dv
-    mac = (C - 1) / 2 * dk + (C + 1) / 2 * dk + C * C / 6 + (C + 1) * dv + 3 * dk * dv
+    mac = (C - 1) / 2 * dk + (C + 1) / 2 * (2 * dk + 2 * dv) + 3 * dk * dv + C * C / 6
     return 2.0 * mac * sh.B * sh.T * sh.H
 
 
@@ -392,6 +402,7 @@ def main():
         cmed = med(cold_t[ck])
         roofline["frac_cold"] = round(kbytes / (cmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         roofline["kernel_us_cold_median"] = round(cmed, 2)
+    mp = None
     if not args.no_measured_peaks:
         mp = measured_peaks(torch, dev, stream)
         if mp is not None:
@@ -413,7 +424,7 @@ def main():
     if not args.no_forward_configs and wid == 4 and not args.prologue and args.variant == "delta":
         del d, ws, x
         torch.cuda.empty_cache()
-        out["forward_configs"] = forward_configs(dn, synth, dev, stream)
+        out["forward_configs"] = forward_configs(dn, synth, dev, stream, mp)
     print(json.dumps(out), flush=True)
 
 
@@ -489,17 +500,25 @@ def _warm_times(fn, stream, reps=20):
     return [a.elapsed_time(b) * 1e3 for a, b in ev]
 
 
-def forward_configs(dn, synth, dev, stream):
+def forward_configs(dn, synth, dev, stream, peaks=None):
     """The forward-only workloads (2, 3 and 5) and the decode step, each timed
     warm (back to back on resident inputs) and cold (a 1 GiB eviction before
-    every call; 20 timed calls, median and minimum), with
-    the fraction of the HBM roofline at its algorithmic bytes."""
+    every call; 20 timed calls, median and minimum), with the fraction of the
+    HBM roofline at its algorithmic bytes, its algorithmic TFLOP/s and GB/s
+    (warm), and, given the machine's measured peaks, the warm fractions of the
+    measured copy bandwidth and bf16 MFMA rate."""
     import torch
     res = {}
     med = lambda v: sorted(v)[len(v) // 2]
 
-    def entry(name, nbytes, tokens, warm, cold, cold_rd):
+    def entry(name, nbytes, tokens, warm, cold, cold_rd, flops):
         floor = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        wmean = sum(warm) / len(warm)
+        extra = {"tflops_warm": round(flops / (wmean * 1e-6) / 1e12, 2),
+                 "gbs_warm": round(nbytes / (wmean * 1e-6) / 1e9, 1)}
+        if peaks is not None:
+            extra["frac_warm_of_measured_copy"] = round(extra["gbs_warm"] / peaks["hbm_copy_GBs"], 4)
+            extra["mfma_frac_warm_of_measured"] = round(extra["tflops_warm"] / peaks["mfma_bf16_TFs"], 4)
         res[name] = {
             "bytes": nbytes, "floor_us": round(floor, 2),
             "warm_us": {"mean": round(sum(warm) / len(warm), 2), "median": round(med(warm), 2),
@@ -510,6 +529,7 @@ def forward_configs(dn, synth, dev, stream):
             "frac_cold": round(floor / med(cold), 4),
             "frac_cold_read_evict": round(floor / med(cold_rd), 4),
             "tokens_per_s_cold": round(tokens / (med(cold) * 1e-6), 1),
+            **extra,
         }
 
     for wid in FWD_WORKLOADS:
@@ -521,7 +541,7 @@ def forward_configs(dn, synth, dev, stream):
         warm = _warm_times(fn, stream)
         cold = _cold_times(fn, stream)
         cold_rd = _cold_times(fn, stream, evict="read")
-        entry(synth.WORKLOAD_NAMES[wid], workload_bytes(sh, False), sh.B * sh.T, warm, cold, cold_rd)
+        entry(synth.WORKLOAD_NAMES[wid], workload_bytes(sh, False), sh.B * sh.T, warm, cold, cold_rd, fwd_flops(sh))
         del d
         torch.cuda.empty_cache()
     x = synth.decode_inputs()
@@ -530,13 +550,13 @@ def forward_configs(dn, synth, dev, stream):
     warm = _warm_times(fn, stream)
     cold = _cold_times(fn, stream)
     cold_rd = _cold_times(fn, stream, evict="read")
-    entry("decode-B256-H32-d128", decode_bytes(), 256, warm, cold, cold_rd)
+    entry("decode-B256-H32-d128", decode_bytes(), 256, warm, cold, cold_rd, decode_flops())
     res["how"] = ("warm: untimed calls for %.0f ms of device time (at least 20), then 20 timed "
                   "back-to-back calls on resident inputs; cold: the same untimed calls, then 20 "
                   "timed calls each after a 1 GiB write (median, min); cold_read_evict: the same "
                   "with a 1 GiB read (a sum) in place of the write, which leaves no dirty lines "
                   "for the timed call to write back; " % WARM_MS +
-                  "frac = the HBM floor at 8 TB/s of the algorithmic bytes over the time; "
+                  "frac = the HBM floor at 8 TB/s of the algorithmic bytes over the time; tflops_warm and gbs_warm = the algorithmic flops and bytes over the warm mean, of_measured against the machine's measured copy and MFMA rates; "
                   "tokens_per_s_cold counts the decode batch as tokens")
     return res
 

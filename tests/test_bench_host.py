@@ -47,3 +47,16 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_algorithmic_flops():
+    # the method's flop counts (GFLOP): the forward workloads 2, 3, 5, the
+    # backward of workload 4 (no recompute) and one decode step of 256 x 32 states
+    g = lambda f: round(f / 1e9, 2)
+    assert [g(bench.fwd_flops(synth.WORKLOADS[w])) for w in (2, 3, 5)] == [36.97, 67.1, 295.73]
+    assert g(bench.bwd_flops(synth.WORKLOADS[4])) == 137.09
+    assert g(bench.decode_flops()) == 0.81
+    # per token-head at dk = 128, dv = 256, C = 64 (MACs): 63/2 128 + 65/2 (256 + 512)
+    # + 3 128 256 + 64^2 / 6
+    mac = 63 / 2 * 128 + 65 / 2 * 768 + 3 * 128 * 256 + 64 * 64 / 6
+    assert bench.fwd_flops(synth.WORKLOADS[3]) == 2 * mac * 4 * 4096 * 16
